@@ -1,0 +1,212 @@
+"""Benchmark of the tree speculative-decoding verify step on one MI355X.
+
+One step = the whole verify hot path over one batch of seeded synthetic input:
+jt_build_tree -> jt_tree_meta -> jt_tree_attention -> jt_accept, all through
+the C ABI on the current stream.  The workload is the Qwen3-30B-A3B-shaped
+attention layer (32 query heads, 4 KV heads, head_dim 128, bf16), batch 8,
+32768-token prefixes in a paged cache (16-token pages, permuted), trees of
+budget B = 256 (W = 8, N = 16) drafted from [16, 151936] fp32 logits, and
+acceptance over [257, 151936] fp32 target logits per sequence.
+
+Printed: one JSON line.  ``value`` is tree-node tokens per second of the whole
+step (sum of n_nodes over the batch / step time); the attention kernel is
+additionally reported as KV GB/s and against the bf16 MFMA roofline.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+WORKLOAD = "qwen3_30b_a3b_b8"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default=WORKLOAD)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seqs", type=int, default=3,
+                    help="sequences of the workload the CPU oracle is timed on")
+    return ap.parse_args()
+
+
+def algorithmic_work(w, prefix, n_nodes, depth):
+    """Attention bytes and flops the method must move / compute.
+
+    bytes = sum_s (P_s + n_s) * Hkv * D * 2 * e   (K and V read once)
+          + sum_s n_s * Hq * D * 2 * e           (Q read, O written)
+    flops = 4 * D * Hq * sum_s sum_{i < n_s} (P_s + depth_i + 1)
+    (masked tail entries do not count).
+    """
+    e = 2 if w.dtype == "bf16" else 4
+    kv = q = fl = 0
+    for s in range(len(prefix)):
+        P, n = int(prefix[s]), int(n_nodes[s])
+        kv += (P + n) * w.hkv * w.head_dim * 2 * e
+        q += n * w.hq * w.head_dim * 2 * e
+        vis = n * P + int(sum(int(d) + 1 for d in depth[s][:n]))
+        fl += 4 * w.head_dim * w.hq * vis
+    return kv, q, fl
+
+
+def cpu_baseline(w, x, seqs):
+    """The CPU oracle, untouched, on the first ``seqs`` sequences of the batch."""
+    import numpy as np
+    from oracle import tree_oracle as O
+    try:
+        import threadpoolctl
+        threads = max([p.get("num_threads", 1) for p in threadpoolctl.threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count() or 1
+    kf = x.k_pool.float().numpy()
+    vf = x.v_pool.float().numpy()
+    t0 = time.perf_counter()
+    nodes = 0
+    for s in range(seqs):
+        tr = O.build_tree(x.draft[s].numpy(), w.width_w, w.budget_b, int(x.root_token[s]),
+                          check_exact=False)
+        n = tr["n_nodes"]
+        O.ancestor_mask(tr["parent"], n)
+        O.tree_attention_seq_fast(x.q[s].float().numpy(), kf, vf, x.page_table[s].numpy(),
+                                  int(x.prefix_len[s]), tr["parent"], n, w.scale)
+        O.accept(x.target[s].numpy(), tr["parent"], tr["token"], tr["depth"], n, w.depth_n)
+        nodes += n
+    dt = time.perf_counter() - t0
+    return {"value": nodes / dt, "unit": "tree-node tok/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{seqs} of {w.batch} sequences of the same workload, whole verify step "
+                      f"(build, mask, attention, accept) in fp64 NumPy; {dt:.2f} s"}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+    from tree_causal_attention_amd import binding as B
+    from tree_causal_attention_amd import workloads as WL
+
+    w = WL.WORKLOADS[args.workload]
+    dev = torch.device("cuda:0")
+    x = WL.make_inputs(w)
+    d_draft = x.draft.to(dev)
+    d_target = x.target.to(dev)
+    d_q, d_k, d_v = x.q.to(dev), x.k_pool.to(dev), x.v_pool.to(dev)
+    d_prefix, d_table, d_root = x.prefix_len.to(dev), x.page_table.to(dev), x.root_token.to(dev)
+    err = torch.zeros(1, dtype=torch.int32, device=dev)
+    b, T = w.batch, w.max_nodes
+
+    # outputs and workspaces allocated once, outside the timed region
+    lib = B.load()
+    ws_build = torch.empty(max(1, lib.jt_build_tree_workspace(b, w.depth_n, w.vocab, w.width_w,
+                                                              w.budget_b)), dtype=torch.uint8,
+                           device=dev)
+    ws_attn = torch.empty(max(1, lib.jt_tree_attention_workspace(
+        b, T, w.hq, w.hkv, w.head_dim, x.page_table.shape[1], 16, B.JT_BF16 if w.dtype == "bf16"
+        else B.JT_F32)), dtype=torch.uint8, device=dev)
+    ws_acc = torch.empty(max(1, lib.jt_accept_workspace(b, T, w.vocab)), dtype=torch.uint8,
+                         device=dev)
+    anc = torch.empty((b, T, (T + 31) // 32), dtype=torch.int32, device=dev)
+    out = torch.empty_like(d_q)
+    lse = torch.empty((b, T, w.hq), dtype=torch.float32, device=dev)
+    stream = torch.cuda.current_stream()
+    ev = {k: [] for k in ("s0", "s1", "s2", "s3", "s4")}
+
+    def step(record):
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s0"].append(e)
+        tree = B.jt_build_tree(d_draft, w.width_w, w.budget_b, d_root, err=err, workspace=ws_build)
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s1"].append(e)
+        B.jt_tree_meta(tree["parent"], tree["n_nodes"], err=err, out=anc)
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s2"].append(e)
+        B.jt_tree_attention(d_q, d_k, d_v, tree["n_nodes"], d_prefix, d_table, x.num_pages, anc,
+                            w.scale, err=err, out=out, lse=lse, workspace=ws_attn)
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s3"].append(e)
+        res = B.jt_accept(d_target, w.depth_n, tree["parent"], tree["token"], tree["depth"],
+                          tree["n_nodes"], err=err, workspace=ws_acc)
+        if record:
+            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s4"].append(e)
+        return tree, res
+
+    for _ in range(args.warmup):
+        step(False)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        tree, res = step(True)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error bits {int(err.item())}")
+
+    def avg(a, b_):
+        return sum(x_.elapsed_time(y_) for x_, y_ in zip(ev[a], ev[b_])) / len(ev[a])
+    stage_ms = {"build_tree": avg("s0", "s1"), "tree_meta": avg("s1", "s2"),
+                "tree_attention": avg("s2", "s3"), "accept": avg("s3", "s4")}
+    ms_step = wall * 1000.0 / args.steps
+    n_nodes = tree["n_nodes"].cpu().numpy()
+    depth = tree["depth"].cpu().numpy()
+    kv_bytes, qo_bytes, flops = algorithmic_work(w, x.prefix_len.numpy(), n_nodes, depth)
+    t_attn = stage_ms["tree_attention"] / 1000.0
+    achieved_tflops = flops / t_attn / 1e12
+    kv_gbps = kv_bytes / t_attn / 1e9
+    tokens = int(n_nodes.sum())
+    result = {
+        "metric": "tree-attn verify tree-node tok/s + KV GB/s at B=256; % of HBM/MFMA peak",
+        "value": tokens / (ms_step / 1000.0),
+        "unit": "tree-node tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded draws with the workload's shapes; no datasets or weights)",
+        "config": {
+            "workload": f"{w.name}: full verify step (build tree, tree meta, paged tree attention, "
+                        f"accept), batch {w.batch}, prefix {w.prefix}, {w.hq}q/{w.hkv}kv heads, "
+                        f"head_dim {w.head_dim}, B={w.budget_b}, W={w.width_w}, N={w.depth_n}, "
+                        f"vocab {w.vocab}, page 16",
+            "tree_nodes_per_step": tokens,
+        },
+        "roofline": {
+            "kernel": "tree_attn_mfma (jt_tree_attention)",
+            "bound": "mfma",
+            "achieved": achieved_tflops,
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": achieved_tflops / PEAK_BF16_TFLOPS,
+            "traffic": None,
+            "algorithmic_flops": flops,
+            "algorithmic_bytes": kv_bytes + qo_bytes,
+        },
+        "kv_gbps": kv_gbps,
+        "kv_hbm_frac": kv_gbps / PEAK_HBM_GBPS,
+        "stage_ms": stage_ms,
+        "accept_len": res[0].cpu().tolist(),
+    }
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(w, x, min(args.cpu_seqs, w.batch))
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

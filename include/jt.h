@@ -1,0 +1,223 @@
+/*
+ * jt.h -- C ABI of the tree speculative-decoding verify step on AMD MI355X
+ * (gfx950).  Four operations, each a thin host entry point that validates its
+ * arguments and enqueues HIP kernels on the caller's stream:
+ *
+ *   jt_build_tree      candidate tree from the draft's per-depth logits
+ *   jt_tree_meta       per-node ancestor bitmasks (the tree-causal mask)
+ *   jt_tree_attention  paged tree-causal attention of every tree node
+ *   jt_accept          greedy acceptance of the longest matching path
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Every pointer argument is DEVICE memory unless marked [host].  The caller
+ *   allocates and owns all buffers, including the workspace; the library
+ *   allocates nothing and keeps no mutable global state, so calls are
+ *   re-entrant and thread-safe.  Calls that share a workspace buffer must be
+ *   ordered on one stream.
+ * - `stream` is a hipStream_t passed as void* (NULL = the legacy default
+ *   stream).  Every call only enqueues work and returns; nothing synchronises
+ *   with the host.  Per-sequence counts (n_nodes, prefix_len) stay on the
+ *   device and are read there.
+ * - Host-side argument checks run before anything is enqueued.  A call that
+ *   returns anything but JT_OK has enqueued nothing and written nothing.
+ *   JT_ERR_LAUNCH means a kernel launch itself failed (the stream state is then
+ *   whatever HIP reports).
+ * - Invalid DEVICE data (which the host cannot see) is reported through the
+ *   optional `err` word: kernels atomically OR the JT_DERR_* bits below into
+ *   *err and skip the offending item without reading out of bounds.  Outputs
+ *   of a skipped item are unspecified.  Pass NULL to skip error reporting.
+ * - Layouts are dense, row-major, in the order the brackets give.
+ * - Node numbering: node 0 is the root (the last accepted token).  Drafted
+ *   nodes 1..n_nodes-1 are numbered in best-first pop order, so
+ *   parent[j] < j for every j >= 1 and parent[0] = -1.  A tree of budget B
+ *   has at most max_nodes = B + 1 nodes.
+ */
+#ifndef JT_H
+#define JT_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  JT_OK = 0,
+  JT_ERR_INVALID_ARG = 1,  /* a null pointer, a negative or inconsistent size */
+  JT_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement    */
+  JT_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than the query says    */
+  JT_ERR_LAUNCH = 4        /* a HIP kernel launch failed                       */
+} jt_status;
+
+typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
+
+/* Device error bits (OR-ed into *err). */
+#define JT_DERR_BAD_LOGIT 1   /* NaN or +inf logit, or a draft row without a finite entry */
+#define JT_DERR_BAD_PARENT 2  /* parent[0] != -1, or parent[j] outside [0, j)              */
+#define JT_DERR_BAD_NNODES 4  /* n_nodes outside [1, max_nodes]                             */
+#define JT_DERR_BAD_PAGE 8    /* a page id outside [0, num_pages)                           */
+#define JT_DERR_BAD_PREFIX 16 /* prefix_len < 0, or prefix_len + n_nodes > pages * 16       */
+#define JT_DERR_BAD_DEPTH 32  /* depth[j] != depth[parent[j]] + 1, or deeper than depth_n   */
+
+/* [host] Static, NUL-terminated description of a status code. */
+const char* jt_status_string(jt_status s);
+
+/* [host] Library ABI version (major * 100 + minor). */
+int jt_version(void);
+
+/* ------------------------------------------------------------------------
+ * jt_build_tree -- per-depth top-W candidates, then best-first expansion.
+ *
+ * Defined by the JetSpec news piece (mlqm.cn/news/158889), paragraph on
+ * building the candidate tree (depth N, width W, budget B; top-W per depth;
+ * greedy expansion by cumulative draft log-probability until the budget is
+ * full) and the JetSpec explainer (techwalker.com, "加速AI思考…"), section 五
+ * (priority queue of candidate nodes keyed by the path's cumulative
+ * log-probability, at most W children per popped node, stop at B nodes).
+ *
+ * Readings fixed here (the pages state no tie rules and no arithmetic):
+ *  - The drafter's logits are per depth: row d-1 of a sequence holds depth d,
+ *    and every depth-d node's children are the same top-W tokens of that row
+ *    (logit descending, then token id ascending).
+ *  - One queue pop adds one candidate (parent node, rank) to the tree; a
+ *    popped node shallower than N then offers its W children.  Pops stop after
+ *    B nodes or when no candidate is left, so
+ *    n_nodes = 1 + min(B, W + W^2 + ... + W^N).
+ *  - score(v) = raw(v) - S_depth(v), where raw is the fp64 sum of the fp32
+ *    logits along the path (root to node), S_d = lse_1 + ... + lse_d (fp64,
+ *    added in depth order) and lse_d the fp64 log-sum-exp of row d.
+ *  - Queue order: score descending, then parent node index ascending, then
+ *    candidate rank ascending.
+ * The per-depth log-sum-exp is an fp64 reduction whose summation order
+ * differs from a sequential one in the last bits, so two candidates of
+ * different depths whose scores are within ~1e-13 may be ordered differently
+ * from a sequential fp64 implementation; parent/token/depth are otherwise an
+ * exact function of the inputs.
+ *
+ *   draft_logits  [batch, depth_n, vocab]   dt = JT_F32 or JT_BF16.  Entries
+ *                                            must be finite or -inf; each row
+ *                                            needs one finite entry.
+ *   root_token    [batch] int32             token of node 0.
+ *   parent, token, depth  [batch, budget_b + 1] int32 (out).  Rows past
+ *                                            n_nodes hold -1.
+ *   score         [batch, budget_b + 1] f64 (out, nullable); -inf padded.
+ *   n_nodes       [batch] int32 (out).
+ *   err           int32 (nullable): JT_DERR_BAD_LOGIT.
+ * Limits: batch >= 0, 1 <= depth_n <= 64, 1 <= width_w <= min(vocab, 16),
+ * 0 <= budget_b <= 1023, vocab >= 1; the per-sequence selection state must
+ * fit one workgroup's LDS (JT_ERR_UNSUPPORTED otherwise; fine for N=16, B=256,
+ * W=8).
+ * ---------------------------------------------------------------------- */
+size_t jt_build_tree_workspace(int batch, int depth_n, int vocab, int width_w, int budget_b);
+jt_status jt_build_tree(const void* draft_logits, jt_dtype dt, int batch, int depth_n,
+                        int vocab, int width_w, int budget_b, const int32_t* root_token,
+                        int32_t* parent, int32_t* token, int32_t* depth, double* score,
+                        int32_t* n_nodes, int32_t* err, void* workspace,
+                        size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * jt_tree_meta -- ancestor-or-self bitmasks of every node.
+ *
+ * The tree-causal rule: a node attends to the prefix and to the nodes of its
+ * own root-to-node branch -- never to siblings' branches or to descendants
+ * (JetSpec news piece, paragraph on the one-forward solution and the
+ * tree-causal attention mask; explainer section 三).  Self-visibility is this
+ * library's reading.
+ *
+ *   parent    [batch, max_nodes] int32      parent[0] = -1, parent[j] in [0, j).
+ *   n_nodes   [batch] int32                 1 <= n_nodes <= max_nodes.
+ *   anc_mask  [batch, max_nodes, ceil(max_nodes / 32)] uint32 (out):
+ *             bit (j % 32) of word j / 32 of row i is set iff node j is i or
+ *             an ancestor of i.  Rows >= n_nodes are zero.
+ *   err       JT_DERR_BAD_PARENT, JT_DERR_BAD_NNODES (that sequence's rows are
+ *             then all zero).
+ * Limits: batch >= 0, 1 <= max_nodes <= 1024.
+ * ---------------------------------------------------------------------- */
+jt_status jt_tree_meta(const int32_t* parent, const int32_t* n_nodes, int batch, int max_nodes,
+                       uint32_t* anc_mask, int32_t* err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * jt_tree_attention -- paged tree-causal attention, one pass over the tree.
+ *
+ * For sequence s, node i < n_nodes[s] and query head h (KV head
+ * g = h / (num_q_heads / num_kv_heads)): the visible keys are the prefix
+ * positions t < P = prefix_len[s] and the tree-tail positions P + j for every
+ * j set in anc_mask row i.  o = softmax(scale * q.k over visible keys) @ v,
+ * lse = natural log of the softmax normaliser.  JetSpec explainer section 七
+ * (paged tree attention: tree mask staged on chip, tree-tail masking, no dense
+ * mask), section 三 (all candidate paths verified in one target forward).
+ *
+ *   q         [batch, max_nodes, num_q_heads, head_dim]  dt (RoPE already
+ *             applied by the caller).
+ *   k_pool, v_pool [num_pages, num_kv_heads, page_size, head_dim]  dt.
+ *             Logical position t of sequence s lives in page
+ *             page_table[s, t / page_size], slot t % page_size.  The tree tail:
+ *             node j's K/V are at position P + j (node-index order) and must be
+ *             finite; slots at or past P + n_nodes are never used (they may
+ *             hold anything, NaN included).
+ *   n_nodes, prefix_len [batch] int32.
+ *   page_table [batch, max_pages_per_seq] int32; entries past
+ *             ceil((P + n_nodes) / page_size) are not read.
+ *   anc_mask  as written by jt_tree_meta for the same max_nodes.
+ *   scale     > 0 and finite (e.g. 1/sqrt(head_dim) if q is unscaled).
+ *   out       [batch, max_nodes, num_q_heads, head_dim]  dt (out); rows
+ *             >= n_nodes are not written.
+ *   lse       [batch, max_nodes, num_q_heads] f32 (out, nullable).
+ *   err       JT_DERR_BAD_NNODES, JT_DERR_BAD_PREFIX (sequence skipped),
+ *             JT_DERR_BAD_PAGE (that page's keys read as zero).
+ * Arithmetic: bf16 inputs use bf16 MFMA with fp32 accumulation, probabilities
+ * rounded to bf16 for the PV product, output rounded to bf16.  f32 inputs are
+ * computed in fp32 throughout.
+ * Limits: head_dim in {64, 128}, page_size == 16, num_q_heads a multiple of
+ * num_kv_heads with num_q_heads / num_kv_heads <= 16, 1 <= max_nodes <= 1024,
+ * max_pages_per_seq >= 1, num_pages >= 1.
+ * ---------------------------------------------------------------------- */
+size_t jt_tree_attention_workspace(int batch, int max_nodes, int num_q_heads, int num_kv_heads,
+                                   int head_dim, int max_pages_per_seq, int page_size,
+                                   jt_dtype dt);
+jt_status jt_tree_attention(const void* q, const void* k_pool, const void* v_pool, jt_dtype dt,
+                            int batch, int max_nodes, int num_q_heads, int num_kv_heads,
+                            int head_dim, const int32_t* n_nodes, const int32_t* prefix_len,
+                            const int32_t* page_table, int max_pages_per_seq, int num_pages,
+                            int page_size, const uint32_t* anc_mask, float scale, void* out,
+                            float* lse, int32_t* err, void* workspace, size_t workspace_bytes,
+                            void* stream);
+
+/* ------------------------------------------------------------------------
+ * jt_accept -- greedy acceptance of the longest consistent path.
+ *
+ * Row r of a sequence's target logits is the target's next-token prediction
+ * after node r; a_r = its argmax (ties to the lowest token id).  The root is
+ * accepted; node v >= 1 is accepted iff its parent is accepted and
+ * token[v] == a_{parent[v]}.  The path ends at the deepest accepted node
+ * (lowest index among equals).  JetSpec news piece (the target verifies the
+ * tree and keeps the longest consistent prefix under the SD acceptance rule);
+ * explainer section 三; SD overview (chooseai.io/news/6515), section on when
+ * lossless decoding fails (temperature 0: a draft token is accepted only if
+ * it equals the target's choice).
+ *
+ *   target_logits [batch, max_nodes, vocab]  dt; rows >= n_nodes not read.
+ *   parent, token, depth [batch, max_nodes] int32 (as from jt_build_tree).
+ *   n_nodes   [batch] int32.
+ *   accept_len   [batch] int32 (out): depth of the deepest accepted node.
+ *   accept_nodes [batch, depth_n] int32 (out): node indices of the accepted
+ *                path (root excluded), -1 padded.
+ *   bonus_token  [batch] int32 (out): a at the deepest accepted node.
+ *   err       JT_DERR_BAD_LOGIT (NaN), JT_DERR_BAD_NNODES, JT_DERR_BAD_PARENT,
+ *             JT_DERR_BAD_DEPTH (that sequence's outputs are then zero / -1).
+ * Limits: batch >= 0, 1 <= max_nodes <= 1024, vocab >= 1, 1 <= depth_n <= 64.
+ * ---------------------------------------------------------------------- */
+size_t jt_accept_workspace(int batch, int max_nodes, int vocab);
+jt_status jt_accept(const void* target_logits, jt_dtype dt, int batch, int max_nodes, int vocab,
+                    int depth_n, const int32_t* parent, const int32_t* token,
+                    const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
+                    int32_t* accept_nodes, int32_t* bonus_token, int32_t* err, void* workspace,
+                    size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* JT_H */

@@ -1,0 +1,122 @@
+"""The C-ABI library loads, exports every entry point include/jt.h declares,
+and rejects invalid arguments on the host before touching the device (no
+compute call happens here; these run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from tree_causal_attention_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "jt.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(jt_[a-z_0-9]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(B.LIB_PATH):
+        from tree_causal_attention_amd import build
+        build.build()
+    return B.load()
+
+
+def test_every_declared_symbol_is_exported(lib):
+    names = _declared()
+    assert {"jt_build_tree", "jt_tree_meta", "jt_tree_attention", "jt_accept"} <= set(names)
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.SIGNATURES), "binding signatures out of sync with jt.h"
+
+
+def test_status_strings(lib):
+    for s in range(5):
+        assert lib.jt_status_string(s)
+    assert lib.jt_version() >= 100
+
+
+N = None
+
+
+def test_build_tree_validation(lib):
+    bt = lib.jt_build_tree
+    ok_args = dict(dt=0, b=1, n=4, v=100, w=4, bb=16)
+
+    def call(dt=0, b=1, n=4, v=100, w=4, bb=16, ws_bytes=0, ptr=1):
+        p = ctypes.c_void_p(ptr) if ptr else None
+        return bt(p, dt, b, n, v, w, bb, p, p, p, p, None, p, None, p, ws_bytes, None)
+
+    assert call(w=101) == B.JT_ERR_INVALID_ARG          # W > V
+    assert call(n=0) == B.JT_ERR_INVALID_ARG
+    assert call(bb=-1) == B.JT_ERR_INVALID_ARG
+    assert call(dt=7) == B.JT_ERR_INVALID_ARG
+    assert call(w=17, v=1000) == B.JT_ERR_UNSUPPORTED    # W > 16
+    assert call(bb=1024) == B.JT_ERR_UNSUPPORTED         # B + 1 > 1024
+    assert call(n=65) == B.JT_ERR_UNSUPPORTED
+    assert call(ptr=0) == B.JT_ERR_INVALID_ARG           # null pointers
+    assert call(ws_bytes=0) == B.JT_ERR_WORKSPACE        # workspace too small
+    assert call(b=0) == B.JT_OK                          # empty batch: nothing to do
+    assert lib.jt_build_tree_workspace(1, 4, 100, 4, 16) > 0
+
+
+def test_tree_meta_validation(lib):
+    f = lib.jt_tree_meta
+    p = ctypes.c_void_p(1)
+    assert f(p, p, 1, 0, p, None, None) == B.JT_ERR_INVALID_ARG
+    assert f(p, p, -1, 4, p, None, None) == B.JT_ERR_INVALID_ARG
+    assert f(p, p, 1, 1025, p, None, None) == B.JT_ERR_UNSUPPORTED
+    assert f(None, p, 1, 4, p, None, None) == B.JT_ERR_INVALID_ARG
+    assert f(None, None, 0, 4, None, None, None) == B.JT_OK
+
+
+def test_tree_attention_validation(lib):
+    f = lib.jt_tree_attention
+    p = ctypes.c_void_p(1)
+
+    def call(dt=1, b=1, T=17, hq=32, hkv=8, D=128, maxp=8, npages=10, ps=16, scale=1.0, ws=1 << 40,
+             ptr=p):
+        return f(ptr, ptr, ptr, dt, b, T, hq, hkv, D, ptr, ptr, ptr, maxp, npages, ps, ptr,
+                 scale, ptr, None, None, ptr, ws, None)
+
+    assert call(hkv=7) == B.JT_ERR_INVALID_ARG           # Hq % Hkv != 0
+    assert call(D=96) == B.JT_ERR_UNSUPPORTED
+    assert call(ps=32) == B.JT_ERR_UNSUPPORTED
+    assert call(T=1025) == B.JT_ERR_UNSUPPORTED
+    assert call(hq=34, hkv=2) == B.JT_ERR_UNSUPPORTED    # group > 16
+    assert call(scale=0.0) == B.JT_ERR_INVALID_ARG
+    assert call(scale=float("nan")) == B.JT_ERR_INVALID_ARG
+    assert call(npages=0) == B.JT_ERR_INVALID_ARG
+    assert call(ptr=None) == B.JT_ERR_INVALID_ARG
+    assert call(b=0) == B.JT_OK
+    need = lib.jt_tree_attention_workspace(1, 17, 32, 8, 128, 8, 16, 1)
+    if need:
+        assert call(ws=need - 1) == B.JT_ERR_WORKSPACE
+
+
+def test_accept_validation(lib):
+    f = lib.jt_accept
+    p = ctypes.c_void_p(1)
+
+    def call(dt=0, b=1, T=17, V=100, N=8, ws=1 << 40, ptr=p):
+        return f(ptr, dt, b, T, V, N, ptr, ptr, ptr, ptr, ptr, ptr, ptr, None, ptr, ws, None)
+
+    assert call(T=0) == B.JT_ERR_INVALID_ARG
+    assert call(N=0) == B.JT_ERR_INVALID_ARG
+    assert call(T=2000) == B.JT_ERR_UNSUPPORTED
+    assert call(ptr=None) == B.JT_ERR_INVALID_ARG
+    assert call(ws=0) == B.JT_ERR_WORKSPACE
+    assert call(b=0) == B.JT_OK
+
+
+def test_workspace_queries_are_consistent(lib):
+    # bigger problems never need less workspace
+    a = lib.jt_accept_workspace(1, 257, 151936)
+    b = lib.jt_accept_workspace(8, 257, 151936)
+    assert 0 < a <= b
+    assert lib.jt_tree_attention_workspace(1, 17, 4, 1, 64, 8, 16, 0) == 0   # fp32: no split

@@ -1,0 +1,172 @@
+"""ctypes binding of ``libjt.so`` (the C ABI declared in include/jt.h).
+
+Argument marshalling only: the functions below take torch tensors that live
+on the GPU, allocate the outputs and the workspace with torch (torch is used
+for device memory and streams), pass raw pointers and the current HIP stream
+to the library, and raise on a non-OK status.  Every step of the computation
+runs in the library's HIP kernels.  There is no fallback: if the library is
+missing or the GPU is absent the calls raise.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libjt.so")
+
+JT_F32, JT_BF16 = 0, 1
+JT_OK, JT_ERR_INVALID_ARG, JT_ERR_UNSUPPORTED, JT_ERR_WORKSPACE, JT_ERR_LAUNCH = range(5)
+DERR_BAD_LOGIT, DERR_BAD_PARENT, DERR_BAD_NNODES, DERR_BAD_PAGE, DERR_BAD_PREFIX, DERR_BAD_DEPTH = (
+    1, 2, 4, 8, 16, 32)
+
+_c_int, _c_size, _vp, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
+
+SIGNATURES = {
+    "jt_status_string": (ctypes.c_char_p, [_c_int]),
+    "jt_version": (_c_int, []),
+    "jt_build_tree_workspace": (_c_size, [_c_int] * 5),
+    "jt_build_tree": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                               _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "jt_tree_meta": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp]),
+    "jt_tree_attention_workspace": (_c_size, [_c_int] * 8),
+    "jt_tree_attention": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                   _vp, _vp, _vp, _c_int, _c_int, _c_int, _vp, _c_float, _vp, _vp,
+                                   _vp, _vp, _c_size, _vp]),
+    "jt_accept_workspace": (_c_size, [_c_int] * 3),
+    "jt_accept": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
+                           _vp, _vp, _vp, _vp, _c_size, _vp]),
+}
+
+
+class JTError(RuntimeError):
+    def __init__(self, fn: str, status: int, msg: str):
+        super().__init__(f"{fn} failed: {msg} (status {status})")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Loads the library once; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build it first "
+                              "(python -c 'import __graft_entry__ as g; g.build()')")
+        lib = ctypes.CDLL(path)
+        for name, (res, args) in SIGNATURES.items():
+            f = getattr(lib, name)
+            f.restype, f.argtypes = res, args
+        _lib = lib
+    return _lib
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream():
+    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+
+
+def _check(fn: str, status: int):
+    if status != JT_OK:
+        raise JTError(fn, status, load().jt_status_string(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.float32:
+        return JT_F32
+    if t.dtype == torch.bfloat16:
+        return JT_BF16
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _cuda(t: torch.Tensor, name: str):
+    if not (t.is_cuda and t.is_contiguous()):
+        raise ValueError(f"{name} must be a contiguous GPU tensor")
+
+
+def _workspace(nbytes: int, device):
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def jt_build_tree(draft_logits: torch.Tensor, width_w: int, budget_b: int,
+                  root_token: torch.Tensor, err: torch.Tensor | None = None,
+                  with_score: bool = True, workspace: torch.Tensor | None = None):
+    """Returns dict(parent, token, depth, score, n_nodes) for a [b, N, V] batch."""
+    lib = load()
+    _cuda(draft_logits, "draft_logits")
+    b, N, V = draft_logits.shape
+    dev = draft_logits.device
+    T = budget_b + 1
+    out = {k: torch.empty((b, T), dtype=torch.int32, device=dev) for k in ("parent", "token", "depth")}
+    out["score"] = torch.empty((b, T), dtype=torch.float64, device=dev) if with_score else None
+    out["n_nodes"] = torch.empty((b,), dtype=torch.int32, device=dev)
+    nbytes = lib.jt_build_tree_workspace(b, N, V, width_w, budget_b)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    _check("jt_build_tree", lib.jt_build_tree(
+        _ptr(draft_logits), _dtype_code(draft_logits), b, N, V, width_w, budget_b, _ptr(root_token),
+        _ptr(out["parent"]), _ptr(out["token"]), _ptr(out["depth"]), _ptr(out["score"]),
+        _ptr(out["n_nodes"]), _ptr(err), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def jt_tree_meta(parent: torch.Tensor, n_nodes: torch.Tensor, err: torch.Tensor | None = None,
+                 out: torch.Tensor | None = None):
+    """Ancestor bitmasks [b, T, ceil(T/32)] as int32 words (uint32 bit patterns)."""
+    lib = load()
+    _cuda(parent, "parent")
+    b, T = parent.shape
+    if out is None:
+        out = torch.empty((b, T, (T + 31) // 32), dtype=torch.int32, device=parent.device)
+    _check("jt_tree_meta", lib.jt_tree_meta(_ptr(parent), _ptr(n_nodes), b, T, _ptr(out),
+                                            _ptr(err), _stream()))
+    return out
+
+
+def jt_tree_attention(q, k_pool, v_pool, n_nodes, prefix_len, page_table, num_pages, anc_mask,
+                      scale: float, err=None, with_lse: bool = True, out=None, lse=None,
+                      workspace=None):
+    """Paged tree attention; returns (out [b, T, Hq, D], lse [b, T, Hq] or None)."""
+    lib = load()
+    for t, nm in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"), (page_table, "page_table")):
+        _cuda(t, nm)
+    b, T, hq, D = q.shape
+    hkv, ps = k_pool.shape[1], k_pool.shape[2]
+    maxp = page_table.shape[1]
+    dt = _dtype_code(q)
+    if out is None:
+        out = torch.empty_like(q)
+    if with_lse and lse is None:
+        lse = torch.empty((b, T, hq), dtype=torch.float32, device=q.device)
+    nbytes = lib.jt_tree_attention_workspace(b, T, hq, hkv, D, maxp, ps, dt)
+    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    _check("jt_tree_attention", lib.jt_tree_attention(
+        _ptr(q), _ptr(k_pool), _ptr(v_pool), dt, b, T, hq, hkv, D, _ptr(n_nodes),
+        _ptr(prefix_len), _ptr(page_table), maxp, int(num_pages), ps, _ptr(anc_mask),
+        float(scale), _ptr(out), _ptr(lse), _ptr(err), _ptr(ws), ws.numel(), _stream()))
+    return out, lse
+
+
+def jt_accept(target_logits, depth_n: int, parent, token, depth, n_nodes, err=None,
+              workspace=None):
+    """Returns (accept_len [b], accept_nodes [b, depth_n], bonus_token [b])."""
+    lib = load()
+    _cuda(target_logits, "target_logits")
+    b, T, V = target_logits.shape
+    dev = target_logits.device
+    alen = torch.empty((b,), dtype=torch.int32, device=dev)
+    anodes = torch.empty((b, depth_n), dtype=torch.int32, device=dev)
+    bonus = torch.empty((b,), dtype=torch.int32, device=dev)
+    nbytes = lib.jt_accept_workspace(b, T, V)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    _check("jt_accept", lib.jt_accept(
+        _ptr(target_logits), _dtype_code(target_logits), b, T, V, depth_n, _ptr(parent),
+        _ptr(token), _ptr(depth), _ptr(n_nodes), _ptr(alen), _ptr(anodes), _ptr(bonus),
+        _ptr(err), _ptr(ws), ws.numel(), _stream()))
+    return alen, anodes, bonus

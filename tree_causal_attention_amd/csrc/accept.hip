@@ -1,0 +1,245 @@
+// jt_accept: greedy acceptance of the longest consistent path.
+//
+// JetSpec news piece (mlqm.cn/news/158889): the target verifies the whole tree
+// in one pass and keeps the longest prefix consistent with the SD acceptance
+// rule; JetSpec explainer section 三 (the longest accepted prefix along each
+// candidate path); SD overview (chooseai.io/news/6515), section on when
+// "lossless" fails: at temperature 0 a draft token is accepted only when it
+// equals the target's choice.
+//
+// row_argmax: one workgroup per (vocab chunk, tree row, sequence) streams the
+//   target logits of rows < n_nodes once with 16-byte loads (HBM-bound) and
+//   keeps the best (value, lowest id).
+// accept_walk: one workgroup per sequence, one thread per node: merges the
+//   chunk winners, marks accepted nodes level by level (parent < child, so a
+//   level only reads the previous one) and picks the deepest accepted node.
+#include "jt_device.h"
+#include "jt_host.h"
+
+#include <algorithm>
+
+namespace jt {
+
+constexpr int kArgmaxThreads = 256;
+constexpr int kWalkThreads = 1024;
+
+template <typename T, int VEC>
+__global__ __launch_bounds__(kArgmaxThreads) void row_argmax(
+    const T* __restrict__ logits, const int32_t* __restrict__ n_nodes, int max_nodes, int vocab,
+    int chunks, int chunk_len, float* __restrict__ part_val, int* __restrict__ part_idx,
+    int32_t* err) {
+  const int c = blockIdx.x, row = blockIdx.y, seq = blockIdx.z;
+  const int n = n_nodes[seq];
+  if (n < 1 || n > max_nodes || row >= n) return;
+  const T* x = logits + (static_cast<size_t>(seq) * max_nodes + row) * vocab;
+  const int begin = c * chunk_len;
+  const int end = min(vocab, begin + chunk_len);
+  float bv = -INFINITY;
+  int bi = INT32_MAX;
+  bool bad = false;
+  if (VEC > 1) {
+    // begin and end are multiples of VEC here (host guarantees vocab % VEC == 0
+    // and chunk_len % VEC == 0), and rows start VEC-aligned.
+    for (int i = begin + threadIdx.x * VEC; i < end; i += kArgmaxThreads * VEC) {
+      float v[VEC];
+      if constexpr (sizeof(T) == 4) {
+        const float4 f = *reinterpret_cast<const float4*>(x + i);
+        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(x + i);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          v[2 * k] = __uint_as_float(w[k] << 16);
+          v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < VEC; ++k) {
+        if (v[k] != v[k]) { bad = true; continue; }
+        if (better(v[k], i + k, bv, bi)) { bv = v[k]; bi = i + k; }
+      }
+    }
+  } else {
+    for (int i = begin + threadIdx.x; i < end; i += kArgmaxThreads) {
+      const float v = load_as_f32(x, i);
+      if (v != v) { bad = true; continue; }
+      if (better(v, i, bv, bi)) { bv = v; bi = i; }
+    }
+  }
+  if (bad) report(err, JT_DERR_BAD_LOGIT);
+  for (int o = 32; o > 0; o >>= 1) {
+    const float ov = shfl_xor(bv, o);
+    const int oi = shfl_xor(bi, o);
+    if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+  }
+  __shared__ float sv[kArgmaxThreads / kWave];
+  __shared__ int si[kArgmaxThreads / kWave];
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  if (lane == 0) { sv[wv] = bv; si[wv] = bi; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int w = 1; w < kArgmaxThreads / kWave; ++w)
+      if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
+    const size_t o = (static_cast<size_t>(seq) * max_nodes + row) * chunks + c;
+    part_val[o] = bv;
+    part_idx[o] = bi;
+  }
+}
+
+__global__ __launch_bounds__(kWalkThreads) void accept_walk(
+    const float* __restrict__ part_val, const int* __restrict__ part_idx, int chunks,
+    int max_nodes, int depth_n, const int32_t* __restrict__ parent,
+    const int32_t* __restrict__ token, const int32_t* __restrict__ depth,
+    const int32_t* __restrict__ n_nodes, int32_t* __restrict__ accept_len,
+    int32_t* __restrict__ accept_nodes, int32_t* __restrict__ bonus_token, int32_t* err) {
+  __shared__ int a[1024];
+  __shared__ int par[1024];
+  __shared__ int dep[1024];
+  __shared__ unsigned char acc[1024];
+  __shared__ int bad;
+  __shared__ unsigned int best_key;
+  const int seq = blockIdx.x, v = threadIdx.x;
+  const int n = n_nodes[seq];
+  int32_t* nodes_out = accept_nodes + static_cast<size_t>(seq) * depth_n;
+  if (n < 1 || n > max_nodes) {
+    if (v == 0) {
+      report(err, JT_DERR_BAD_NNODES);
+      accept_len[seq] = 0;
+      bonus_token[seq] = -1;
+    }
+    for (int k = v; k < depth_n; k += kWalkThreads) nodes_out[k] = -1;
+    return;
+  }
+  if (v == 0) { bad = 0; best_key = 0u; }
+  __syncthreads();
+  const size_t base = static_cast<size_t>(seq) * max_nodes;
+  if (v < n) {
+    const size_t o = (base + v) * chunks;
+    float bv = part_val[o];
+    int bi = part_idx[o];
+    for (int c = 1; c < chunks; ++c)
+      if (better(part_val[o + c], part_idx[o + c], bv, bi)) { bv = part_val[o + c]; bi = part_idx[o + c]; }
+    a[v] = bi;
+    par[v] = parent[base + v];
+    dep[v] = depth[base + v];
+    acc[v] = (v == 0) ? 1 : 0;
+  }
+  __syncthreads();
+  if (v < n) {
+    int b = 0;
+    if (v == 0) {
+      if (par[0] != -1 || dep[0] != 0) b = JT_DERR_BAD_PARENT;
+    } else {
+      const int p = par[v];
+      if (p < 0 || p >= v) b = JT_DERR_BAD_PARENT;
+      else if (dep[v] != dep[p] + 1 || dep[v] > depth_n) b = JT_DERR_BAD_DEPTH;
+    }
+    if (b) atomicOr(&bad, b);
+  }
+  __syncthreads();
+  if (bad) {
+    if (v == 0) {
+      report(err, bad);
+      accept_len[seq] = 0;
+      bonus_token[seq] = -1;
+    }
+    for (int k = v; k < depth_n; k += kWalkThreads) nodes_out[k] = -1;
+    return;
+  }
+  for (int lvl = 1; lvl <= depth_n; ++lvl) {
+    if (v < n && dep[v] == lvl) {
+      const int p = par[v];
+      acc[v] = (acc[p] && token[base + v] == a[p]) ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  if (v < n && acc[v])
+    atomicMax(&best_key, (static_cast<unsigned int>(dep[v]) << 16) | (0xFFFFu - v));
+  __syncthreads();
+  if (v == 0) {
+    const int end = static_cast<int>(0xFFFFu - (best_key & 0xFFFFu));
+    const int L = dep[end];
+    int u = end;
+    for (int k = L - 1; k >= 0; --k) { nodes_out[k] = u; u = par[u]; }
+    for (int k = L; k < depth_n; ++k) nodes_out[k] = -1;
+    accept_len[seq] = L;
+    bonus_token[seq] = a[end];
+  }
+}
+
+// ------------------------------------------------------------------ host side
+
+struct ArgmaxPlan {
+  int chunks, chunk_len, vec;
+};
+
+static ArgmaxPlan argmax_plan(int batch, int max_nodes, int vocab, int vec_elems) {
+  ArgmaxPlan p{};
+  const long long rows = static_cast<long long>(batch) * max_nodes;
+  const int by_rows = static_cast<int>(std::max<long long>(1, (2048 + rows - 1) / std::max<long long>(1, rows)));
+  const int by_vocab = std::max(1, (vocab + 4095) / 4096);
+  p.chunks = std::min(64, std::min(by_rows, by_vocab));
+  p.vec = (vocab % vec_elems == 0) ? vec_elems : 1;
+  int len = (vocab + p.chunks - 1) / p.chunks;
+  len = (len + p.vec - 1) / p.vec * p.vec;
+  p.chunk_len = len;
+  p.chunks = (vocab + len - 1) / len;
+  return p;
+}
+
+static void argmax_ws(int batch, int max_nodes, const ArgmaxPlan& p, size_t* off_idx,
+                      size_t* bytes) {
+  const size_t n = static_cast<size_t>(batch) * max_nodes * p.chunks;
+  const size_t a = (n * sizeof(float) + 255) / 256 * 256;
+  *off_idx = a;
+  *bytes = a + (n * sizeof(int) + 255) / 256 * 256;
+}
+
+size_t accept_workspace_bytes(int batch, int max_nodes, int vocab) {
+  if (batch <= 0) return 0;
+  // the f32 plan has the most chunks of the two dtypes' plans
+  const ArgmaxPlan p4 = argmax_plan(batch, max_nodes, vocab, 4);
+  const ArgmaxPlan p8 = argmax_plan(batch, max_nodes, vocab, 8);
+  size_t o, b4, b8;
+  argmax_ws(batch, max_nodes, p4, &o, &b4);
+  argmax_ws(batch, max_nodes, p8, &o, &b8);
+  return std::max(b4, b8);
+}
+
+template <typename T, int VEC>
+static void launch_argmax(const void* logits, int batch, int max_nodes, int vocab,
+                          const ArgmaxPlan& p, const int32_t* n_nodes, float* pv, int* pi,
+                          int32_t* err, hipStream_t stream) {
+  hipLaunchKernelGGL((row_argmax<T, VEC>), dim3(p.chunks, max_nodes, batch), dim3(kArgmaxThreads),
+                     0, stream, static_cast<const T*>(logits), n_nodes, max_nodes, vocab, p.chunks,
+                     p.chunk_len, pv, pi, err);
+}
+
+hipError_t accept_launch(const void* logits, jt_dtype dt, int batch, int max_nodes, int vocab,
+                         int depth_n, const int32_t* parent, const int32_t* token,
+                         const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
+                         int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
+                         void* workspace, hipStream_t stream) {
+  ArgmaxPlan p = argmax_plan(batch, max_nodes, vocab, dt == JT_F32 ? 4 : 8);
+  if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) p.vec = 1;  // rows not 16-byte aligned
+  size_t off_idx, bytes;
+  argmax_ws(batch, max_nodes, p, &off_idx, &bytes);
+  float* pv = static_cast<float*>(workspace);
+  int* pi = reinterpret_cast<int*>(static_cast<unsigned char*>(workspace) + off_idx);
+  if (dt == JT_F32) {
+    if (p.vec == 4) launch_argmax<float, 4>(logits, batch, max_nodes, vocab, p, n_nodes, pv, pi, err, stream);
+    else launch_argmax<float, 1>(logits, batch, max_nodes, vocab, p, n_nodes, pv, pi, err, stream);
+  } else {
+    if (p.vec == 8) launch_argmax<uint16_t, 8>(logits, batch, max_nodes, vocab, p, n_nodes, pv, pi, err, stream);
+    else launch_argmax<uint16_t, 1>(logits, batch, max_nodes, vocab, p, n_nodes, pv, pi, err, stream);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(accept_walk, dim3(batch), dim3(kWalkThreads), 0, stream, pv, pi, p.chunks,
+                     max_nodes, depth_n, parent, token, depth, n_nodes, accept_len, accept_nodes,
+                     bonus_token, err);
+  return hipGetLastError();
+}
+
+}  // namespace jt
