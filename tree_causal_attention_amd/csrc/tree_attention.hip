@@ -4,25 +4,29 @@
 // never a dense mask; section 三: all candidate paths verified in one target
 // forward; JetSpec news piece, mlqm.cn/news/158889: the tree-causal mask).
 //
-// bf16 path (tree_attn_mfma): one workgroup = 4 waves x 32 query rows for one
-// (sequence, KV head, row tile, key split).  Query rows are (node, head of the
-// GQA group) pairs, node-major, so every K/V tile staged in LDS is reused by
-// all the group's query heads and tree nodes.  Per 64-key tile:
-//   * K and V of 4 pages are gathered from the paged pool with 16-byte loads
-//     (register double buffering), K stored [key][dim] with an XOR swizzle, V
-//     stored transposed [dim][key] with an XOR swizzle;
+// bf16 path (tree_attn_mfma): one workgroup = 8 waves x 32 query rows (two
+// waves per SIMD) for one (sequence, KV head, row tile, key split).  Query rows
+// are (node, head of the GQA group) pairs, node-major, so every K/V tile staged
+// in LDS is reused by all the group's query heads and tree nodes.
+//   * The page ids of the item's key range are staged in LDS first, so tile
+//     loads never wait on a page-table lookup.
+//   * K and V of 4 pages (64 keys) are gathered with 16-byte loads one tile
+//     ahead (register staging) and stored row-major [key][dim] in LDS with a
+//     16-byte-chunk XOR swizzle (chunk ^ key % 8) against bank conflicts.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys as M, queries as N, so
-//     each lane owns one query column and the softmax reductions stay
-//     in-lane plus one cross-half exchange);
-//   * online softmax in base 2 with a lazy rescale (the running max is only
-//     moved when a tile exceeds it by more than 2^8);
-//   * O^T += V^T P^T on the same MFMA, P taken straight from the S^T
-//     registers (the key order inside each 16-key step is permuted to match
-//     the accumulator layout, and V^T is read in the same order).
+//     each lane owns one query column and the softmax reductions stay in-lane
+//     plus one cross-half exchange); Q stays in registers.
+//   * Online softmax in base 2 with a lazy rescale (the running max only
+//     moves when a tile exceeds it by more than 2^8).
+//   * O^T += V^T P^T on the same MFMA.  P comes straight from the S^T
+//     registers (the key order inside each 16-key step is permuted to match the
+//     accumulator layout); the V^T operand is read from the row-major V tile
+//     with ds_read_tr16_b64 transposing loads in the same key order.
 // Only tiles that reach the tree tail apply the mask: the lane's node reads a
-// 64-bit window of its ancestor bitmask.  Tail tiles past the tile's last node
-// are skipped (a node never sees a later node).  Long key ranges are split
-// across workgroups; a combine kernel merges the partial (o, lse) pairs.
+// 64-bit window of its ancestor bitmask.  Tail tiles past the row tile's last
+// node are skipped (a node never sees a later node).  Work items of one
+// (sequence, KV head) share an XCD; long key ranges and the small last row
+// tile are split across workgroups and merged by a combine kernel.
 //
 // f32 path (tree_attn_f32): one wave per (sequence, node, query head), keys
 // across lanes; exact fp32 arithmetic, used for fp32 inputs.
@@ -36,16 +40,29 @@ namespace jt {
 
 typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef i16x4 __attribute__((address_space(3))) * lds_i16x4_ptr;
 
-constexpr int kKT = 64;            // keys per tile
-constexpr int kWavesM = 4;         // waves per workgroup
-constexpr int kRowsWave = 32;      // query rows per wave
-constexpr int kRowsWG = kWavesM * kRowsWave;
-constexpr int kAttnThreads = kWavesM * kWave;
+constexpr int kKT = 64;              // keys per tile
+constexpr int kWavesWG = 8;          // waves per workgroup (2 per SIMD)
+constexpr int kRowsWave = 32;        // query rows per wave
+constexpr int kRowsWG = kWavesWG * kRowsWave;
+constexpr int kAttnThreads = kWavesWG * kWave;
+constexpr int kMaxPagesLds = 4096;   // page ids staged per work item
+constexpr int kMaxTilesItem = kMaxPagesLds * kPage / kKT;
+constexpr int kXcds = 8;             // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;
 
+// Work decomposition (identical for every (sequence, KV head) group; a
+// group's actual row count and key range are read on the device):
+//   rows of a group = n_nodes * group size, in row tiles of 256;
+//   the rt_full full tiles are cut into s_full key splits each, the partial
+//   last tile (if any) into s_part splits;
+//   every group's items sit on one XCD (group sg -> XCD sg % 8) so the K/V
+//   tiles its row tiles share are fetched once into that XCD's L2; within an
+//   XCD the full-tile items are dealt before the cheaper partial-tile ones.
 struct AttnArgs {
   const uint16_t* q;
   const uint16_t* k_pool;
@@ -56,14 +73,14 @@ struct AttnArgs {
   const uint32_t* anc;
   uint16_t* out;
   float* lse;
-  float* part_o;    // [batch, hkv, splits, rows_pad, D] (splits > 1)
-  float* part_lse;  // [batch, hkv, splits, rows_pad]
+  float* part_o;    // partial rows [ngroups * part_rows_group, D]
+  float* part_lse;  // [ngroups * part_rows_group]
   int32_t* err;
-  int max_nodes, hq, hkv, group, max_pages, num_pages, splits, row_tiles, rows_pad, nwords;
+  int max_nodes, hq, hkv, group, max_pages, num_pages, nwords;
+  int rt_full, s_full, s_part, has_partial, items_full, items_part;
+  int ngroups, part_rows_group, full_part_rows;
   float scale_log2;  // scale * log2(e)
 };
-
-__device__ __forceinline__ int vt_swz(int d) { return ((d >> 3) + 2 * (d & 7)) & 15; }
 
 // Validates one sequence; returns false (and reports) when it must be skipped.
 __device__ __forceinline__ bool seq_ok(int n, int P, int max_nodes, int max_pages, int32_t* err,
@@ -79,36 +96,89 @@ __device__ __forceinline__ bool seq_ok(int n, int P, int max_nodes, int max_page
   return true;
 }
 
+struct Item {
+  int s, g, sg, rt, sp, splits;
+};
+
+// Maps the linear workgroup id to a work item; false for padding slots.
+__device__ __forceinline__ bool decode_item(const AttnArgs& a, int L, Item& it) {
+  const int xcd = L % kXcds, slot = L / kXcds;
+  const int gx = (a.ngroups - xcd + kXcds - 1) / kXcds;  // groups owned by this XCD
+  int j;
+  if (slot < gx * a.items_full) {
+    j = slot / a.items_full;
+    const int i = slot % a.items_full;
+    it.rt = i / a.s_full;
+    it.sp = i % a.s_full;
+    it.splits = a.s_full;
+  } else {
+    const int s2 = slot - gx * a.items_full;
+    if (a.items_part == 0 || s2 >= gx * a.items_part) return false;
+    j = s2 / a.items_part;
+    it.rt = a.rt_full;
+    it.sp = s2 % a.items_part;
+    it.splits = a.s_part;
+  }
+  it.sg = xcd + kXcds * j;
+  it.s = it.sg / a.hkv;
+  it.g = it.sg % a.hkv;
+  return true;
+}
+
+// Row offset of a (row tile, split) inside its group's partial block.
+__device__ __forceinline__ int part_row(const AttnArgs& a, int rt, int sp) {
+  if (rt < a.rt_full) return (rt * a.s_full + sp) * kRowsWG;
+  return a.full_part_rows + sp * kRowsWG;
+}
+
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   constexpr int CPK = D / 8;                 // 16-byte chunks per key row
-  constexpr int KLD = kKT * CPK / kAttnThreads;  // K chunk loads per thread
-  constexpr int VQ = kKT / 4;                // key quads per tile
-  constexpr int VTHREADS = VQ * CPK;         // threads that stage V
+  constexpr int LPT = kKT * CPK / kAttnThreads;  // chunks per thread per tensor per tile
   constexpr int DB = D / 32;                 // 32-row blocks of O^T
-  constexpr int KS = D / 16;                 // MFMA k-steps of QK^T
+  constexpr int KS = D / 16;                 // MFMA k-steps of K Q^T
 
   __shared__ __align__(16) uint16_t k_lds[2][kKT * D];
-  __shared__ __align__(16) uint16_t vt_lds[2][D * kKT];
+  __shared__ __align__(16) uint16_t v_lds[2][kKT * D];
+  __shared__ int pg_lds[kMaxPagesLds];
 
-  const int s = blockIdx.z, g = blockIdx.y;
-  const int rt = blockIdx.x / a.splits, sp = blockIdx.x % a.splits;
+  Item item;
+  if (!decode_item(a, blockIdx.x, item)) return;
+  const int s = item.s, g = item.g;
   const int tid = threadIdx.x, lane = tid % kWave, w = tid / kWave;
   const int h = lane >> 5, col = lane & 31;
 
   const int n = a.n_nodes[s];
   const int P = a.prefix_len[s];
-  if (!seq_ok(n, P, a.max_nodes, a.max_pages, a.err, blockIdx.x == 0 && g == 0 && tid == 0)) return;
+  if (!seq_ok(n, P, a.max_nodes, a.max_pages, a.err,
+              g == 0 && item.rt == 0 && item.sp == 0 && tid == 0))
+    return;
   const int rows = n * a.group;
-  const int rowbase = rt * kRowsWG;
+  const int rowbase = item.rt * kRowsWG;
   if (rowbase >= rows) return;
-  const int node_hi = min(n - 1, (rowbase + kRowsWG - 1) / a.group);
-  const int key_end = P + node_hi + 1;                 // causal skip of later nodes
+  const int node_hi = (min(rows, rowbase + kRowsWG) - 1) / a.group;
+  const int key_end = P + node_hi + 1;  // later nodes are never visible to this tile
   const int ntiles = (key_end + kKT - 1) / kKT;
-  const int tb = static_cast<int>(static_cast<long long>(ntiles) * sp / a.splits);
-  const int te = static_cast<int>(static_cast<long long>(ntiles) * (sp + 1) / a.splits);
+  const int tb = static_cast<int>(static_cast<long long>(ntiles) * item.sp / item.splits);
+  const int te = static_cast<int>(static_cast<long long>(ntiles) * (item.sp + 1) / item.splits);
 
-  // ---- this lane's query row
+  // ---- page ids of this item's key range, staged in LDS
+  const int kv_len = P + n;
+  const int pg0 = tb * (kKT / kPage);
+  const int npg = max(0, min(te * (kKT / kPage), (kv_len + kPage - 1) / kPage) - pg0);
+  {
+    const int32_t* ptab = a.page_table + static_cast<size_t>(s) * a.max_pages;
+    for (int i = tid; i < npg; i += kAttnThreads) {
+      int p = ptab[pg0 + i];
+      if (p < 0 || p >= a.num_pages) {
+        report(a.err, JT_DERR_BAD_PAGE);
+        p = -1;
+      }
+      pg_lds[i] = p;
+    }
+  }
+
+  // ---- this lane's query row (B operand of K Q^T, kept in registers)
   const int r = rowbase + w * kRowsWave + col;
   const bool row_ok = r < rows;
   const int node = row_ok ? r / a.group : 0;
@@ -124,75 +194,13 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
     }
   }
   const uint32_t* anc_row = a.anc + (static_cast<size_t>(s) * a.max_nodes + node) * a.nwords;
-
-  const int32_t* ptab = a.page_table + static_cast<size_t>(s) * a.max_pages;
-  const size_t head_stride = static_cast<size_t>(kPage) * D;           // one page of one head
+  const size_t head_stride = static_cast<size_t>(kPage) * D;
   const size_t page_stride = static_cast<size_t>(a.hkv) * head_stride;
+  const uint16_t* kbase = a.k_pool + g * head_stride;
+  const uint16_t* vbase = a.v_pool + g * head_stride;
 
-  // ---- global -> register staging of one tile
-  uint4 kst[KLD];
-  uint4 vst[4];
-  auto fetch = [&](int t0) {
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int e = tid + i * kAttnThreads;
-      const int key = e / CPK, c = e % CPK;
-      const int t = t0 + key;
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (t < P + n) {
-        const int page = ptab[t / kPage];
-        if (page >= 0 && page < a.num_pages) {
-          u = *reinterpret_cast<const uint4*>(a.k_pool + page * page_stride + g * head_stride +
-                                               (t % kPage) * D + c * 8);
-        } else {
-          report(a.err, JT_DERR_BAD_PAGE);
-        }
-      }
-      kst[i] = u;
-    }
-    if (tid < VTHREADS) {
-      const int c = tid % CPK, kq = tid / CPK;
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int t = t0 + 4 * kq + j;
-        uint4 u = make_uint4(0, 0, 0, 0);
-        if (t < P + n) {
-          const int page = ptab[t / kPage];
-          if (page >= 0 && page < a.num_pages)
-            u = *reinterpret_cast<const uint4*>(a.v_pool + page * page_stride + g * head_stride +
-                                                 (t % kPage) * D + c * 8);
-        }
-        vst[j] = u;
-      }
-    }
-  };
-  auto stash = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < KLD; ++i) {
-      const int e = tid + i * kAttnThreads;
-      const int key = e / CPK, c = e % CPK;
-      *reinterpret_cast<uint4*>(&k_lds[buf][key * D + ((c ^ (key & 7)) * 8)]) = kst[i];
-    }
-    if (tid < VTHREADS) {
-      const int c = tid % CPK, kq = tid / CPK;
-      const uint32_t* v0 = reinterpret_cast<const uint32_t*>(&vst[0]);
-      const uint32_t* v1 = reinterpret_cast<const uint32_t*>(&vst[1]);
-      const uint32_t* v2 = reinterpret_cast<const uint32_t*>(&vst[2]);
-      const uint32_t* v3 = reinterpret_cast<const uint32_t*>(&vst[3]);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * c + e;
-        const int sh = (e & 1) ? 16 : 0;
-        const uint32_t x0 = (v0[e >> 1] >> sh) & 0xFFFFu, x1 = (v1[e >> 1] >> sh) & 0xFFFFu;
-        const uint32_t x2 = (v2[e >> 1] >> sh) & 0xFFFFu, x3 = (v3[e >> 1] >> sh) & 0xFFFFu;
-        uint2 pk;
-        pk.x = x0 | (x1 << 16);
-        pk.y = x2 | (x3 << 16);
-        const int pq = kq ^ vt_swz(d);
-        *reinterpret_cast<uint2*>(&vt_lds[buf][d * kKT + pq * 4]) = pk;
-      }
-    }
-  };
+  // lane roles of the transposed V reads (groups of 16 lanes)
+  const int tg = lane >> 4, tk = (lane >> 2) & 3, tq = lane & 3;
 
   f32x16 o_acc[DB];
 #pragma unroll
@@ -202,54 +210,76 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   float m_run = -INFINITY;  // running max in scaled (log2) units
   float l_run = 0.0f;       // this lane's half of the normaliser
 
-  if (tb < te) {
-    fetch(tb * kKT);
-    stash(0);
-  }
-  __syncthreads();
-  for (int it = tb; it < te; ++it) {
-    const int buf = (it - tb) & 1;
-    const int t0 = it * kKT;
-    if (it + 1 < te) fetch(t0 + kKT);
+  // ---- global -> registers -> LDS (two tiles in flight)
+  uint4 kreg[LPT], vreg[LPT];
+  auto fetch = [&](int t0, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) {
+#pragma unroll
+    for (int c = 0; c < LPT; ++c) {
+      const int e = tid + c * kAttnThreads;
+      const int key = e / CPK, ch = e % CPK;
+      const int t = t0 + key;
+      uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
+      if (t < kv_len) {
+        const int p = pg_lds[t / kPage - pg0];
+        if (p >= 0) {
+          const size_t off = p * page_stride + (t % kPage) * D + ch * 8;
+          ku = *reinterpret_cast<const uint4*>(kbase + off);
+          vu = *reinterpret_cast<const uint4*>(vbase + off);
+        }
+      }
+      kr[c] = ku;
+      vr[c] = vu;
+    }
+  };
+  auto stash = [&](int buf, const uint4 (&kr)[LPT], const uint4 (&vr)[LPT]) {
+#pragma unroll
+    for (int c = 0; c < LPT; ++c) {
+      const int e = tid + c * kAttnThreads;
+      const int key = e / CPK, ch = e % CPK;
+      const int o = key * D + ((ch ^ (key & 7)) * 8);
+      *reinterpret_cast<uint4*>(&k_lds[buf][o]) = kr[c];
+      *reinterpret_cast<uint4*>(&v_lds[buf][o]) = vr[c];
+    }
+  };
 
-    // ---- S^T = K Q^T for 2 blocks of 32 keys
+  auto compute = [&](int buf, int t0) {
+    // ---- S^T = K Q^T for 2 blocks of 32 keys (independent accumulators interleaved)
     f32x16 sacc[2];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) sacc[kb][v] = 0.0f;
-      const int key = kb * 32 + col;
 #pragma unroll
-      for (int kk = 0; kk < KS; ++kk) {
+    for (int kk = 0; kk < KS; ++kk) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = kb * 32 + col;
         const int c = 2 * kk + h;
-        const bf16x8 kf = *reinterpret_cast<const bf16x8*>(&k_lds[buf][key * D + ((c ^ (key & 7)) * 8)]);
+        const bf16x8 kf =
+            *reinterpret_cast<const bf16x8*>(&k_lds[buf][key * D + ((c ^ (key & 7)) * 8)]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kk], sacc[kb], 0, 0, 0);
       }
     }
 
-    // ---- mask (tiles that reach the tree tail)
+    // ---- mask (only tiles that reach the tree tail)
     if (t0 + kKT > P) {
       const int jb = t0 - P;  // tail index of the tile's first key (may be < 0)
-      uint64_t win = 0;
-      {
-        const int w0 = (jb >= 0) ? (jb >> 5) : -((-jb + 31) >> 5);
-        const int sh = jb - 32 * w0;  // 0..31
-        uint32_t wd[3];
+      const int w0 = (jb >= 0) ? (jb >> 5) : -((-jb + 31) >> 5);
+      const int sh = jb - 32 * w0;  // 0..31
+      uint32_t wd[3];
 #pragma unroll
-        for (int k = 0; k < 3; ++k) {
-          const int wi = w0 + k;
-          wd[k] = (row_ok && wi >= 0 && wi < a.nwords) ? anc_row[wi] : 0u;
-        }
-        const uint64_t lo = (static_cast<uint64_t>(wd[1]) << 32) | wd[0];
-        win = (lo >> sh) | (sh ? (static_cast<uint64_t>(wd[2]) << (64 - sh)) : 0ull);
+      for (int k = 0; k < 3; ++k) {
+        const int wi = w0 + k;
+        wd[k] = (row_ok && wi >= 0 && wi < a.nwords) ? anc_row[wi] : 0u;
       }
+      const uint64_t lo = (static_cast<uint64_t>(wd[1]) << 32) | wd[0];
+      const uint64_t win = (lo >> sh) | (sh ? (static_cast<uint64_t>(wd[2]) << (64 - sh)) : 0ull);
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int v = 0; v < 16; ++v) {
           const int o = kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          const int t = t0 + o;
-          const bool vis = (t < P) || ((win >> o) & 1ull);
+          const bool vis = (t0 + o < P) || ((win >> o) & 1ull);
           if (!vis) sacc[kb][v] = -INFINITY;
         }
     }
@@ -262,10 +292,12 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
       for (int v = 0; v < 16; ++v) mx = fmaxf(mx, sacc[kb][v]);
     mx = fmaxf(mx, __shfl_xor(mx, 32, kWave));
     const float mx_s = mx * a.scale_log2;
-    const bool need = (m_run == -INFINITY) ? (mx_s != -INFINITY) : (mx_s > m_run + kRescaleThreshold);
+    const bool need =
+        (m_run == -INFINITY) ? (mx_s != -INFINITY) : (mx_s > m_run + kRescaleThreshold);
     if (__builtin_amdgcn_ballot_w64(need)) {
       const float m_new = need ? mx_s : m_run;
-      const float alpha = need ? ((m_run == -INFINITY) ? 0.0f : exp2f(m_run - m_new)) : 1.0f;
+      const float alpha =
+          need ? ((m_run == -INFINITY) ? 0.0f : __builtin_amdgcn_exp2f(m_run - m_new)) : 1.0f;
 #pragma unroll
       for (int db = 0; db < DB; ++db)
 #pragma unroll
@@ -279,50 +311,68 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int v = 0; v < 16; ++v) {
-        const float p = exp2f(fmaf(sacc[kb][v], a.scale_log2, -base));
+        const float p = __builtin_amdgcn_exp2f(fmaf(sacc[kb][v], a.scale_log2, -base));
         l_run += p;
         pf[kb * 2 + (v >> 3)][v & 7] = static_cast<__bf16>(p);
       }
 
-    // ---- O^T += V^T P^T
+    // ---- O^T += V^T P^T; V^T fragments come from the row-major V tile through
+    // transposing LDS reads: in each 16-lane group, lane i gets 4 consecutive
+    // keys at head dim d0 + i when its 16 lanes point at (key k, dims 4q..4q+3).
 #pragma unroll
-    for (int db = 0; db < DB; ++db) {
-      const int d = db * 32 + col;
-      const int sw = vt_swz(d);
+    for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) {
-        const int kb = ks >> 1, j = ks & 1;
-        const int qa = 8 * kb + 4 * j + h;
-        const int qb = qa + 2;
-        const uint2 lo = *reinterpret_cast<const uint2*>(&vt_lds[buf][d * kKT + (qa ^ sw) * 4]);
-        const uint2 hi = *reinterpret_cast<const uint2*>(&vt_lds[buf][d * kKT + (qb ^ sw) * 4]);
-        const uint4 u = make_uint4(lo.x, lo.y, hi.x, hi.y);
+      for (int db = 0; db < DB; ++db) {
+        const int dst = 32 * db + 16 * (tg & 1) + 4 * tq;
+        const int ch = dst >> 3, off = dst & 7;
+        const int ka = 16 * ks + 4 * h + tk;
+        const int kc = ka + 8;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_ptr)(&v_lds[buf][ka * D + ((ch ^ (ka & 7)) * 8) + off]));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (lds_i16x4_ptr)(&v_lds[buf][kc * D + ((ch ^ (kc & 7)) * 8) + off]));
+        const uint2 ulo = __builtin_bit_cast(uint2, lo);
+        const uint2 uhi = __builtin_bit_cast(uint2, hi);
+        const uint4 u = make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
         o_acc[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, u), pf[ks],
                                                             o_acc[db], 0, 0, 0);
       }
     }
+  };
 
-    if (it + 1 < te) stash(buf ^ 1);
+  __syncthreads();  // page ids visible
+  // Iteration it computes tile it from LDS buffer (it - tb) & 1 while tile it+1
+  // is loading into registers; it is stored to the other buffer afterwards.
+  if (tb < te) {
+    fetch(tb * kKT, kreg, vreg);
+    stash(0, kreg, vreg);
+  }
+  __syncthreads();
+  for (int it = tb; it < te; ++it) {
+    const int buf = (it - tb) & 1;
+    if (it + 1 < te) fetch((it + 1) * kKT, kreg, vreg);
+    compute(buf, it * kKT);
+    if (it + 1 < te) stash(buf ^ 1, kreg, vreg);
     __syncthreads();
   }
 
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
   const float inv = (l_tot > 0.0f) ? 1.0f / l_tot : 0.0f;
-  const float lse_v = (l_tot > 0.0f) ? (m_run + log2f(l_tot)) * kLn2 : -INFINITY;
+  const float lse_v = (l_tot > 0.0f) ? (m_run + __builtin_amdgcn_logf(l_tot)) * kLn2 : -INFINITY;
   if (!row_ok) return;
-  if (a.splits == 1) {
+  if (item.splits == 1) {
     uint16_t* op = a.out + ((static_cast<size_t>(s) * a.max_nodes + node) * a.hq + hq) * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const int d0 = db * 32 + 8 * grp + 4 * h;
-        uint2 pk;
         const __bf16 b0 = static_cast<__bf16>(o_acc[db][4 * grp + 0] * inv);
         const __bf16 b1 = static_cast<__bf16>(o_acc[db][4 * grp + 1] * inv);
         const __bf16 b2 = static_cast<__bf16>(o_acc[db][4 * grp + 2] * inv);
         const __bf16 b3 = static_cast<__bf16>(o_acc[db][4 * grp + 3] * inv);
+        uint2 pk;
         pk.x = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b0)) |
                (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b1)) << 16);
         pk.y = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b2)) |
@@ -332,7 +382,8 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
     if (a.lse && h == 0)
       a.lse[(static_cast<size_t>(s) * a.max_nodes + node) * a.hq + hq] = lse_v;
   } else {
-    const size_t prow = ((static_cast<size_t>(s) * a.hkv + g) * a.splits + sp) * a.rows_pad + r;
+    const size_t prow = static_cast<size_t>(item.sg) * a.part_rows_group +
+                        part_row(a, item.rt, item.sp) + (r - rowbase);
     float* op = a.part_o + prow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
@@ -347,28 +398,34 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   }
 }
 
-// Merges the per-split partials of every (sequence, KV head, row).
+// Merges the per-split partials of the row tiles that were split.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine(AttnArgs a) {
   constexpr int TPR = 64;  // threads per row
   constexpr int PER = D / TPR;
-  const int s = blockIdx.z, g = blockIdx.y;
-  const int r = blockIdx.x * (256 / TPR) + threadIdx.x / TPR;
+  const int ctiles_full = a.s_full > 1 ? a.rt_full : 0;
+  const int ctile = blockIdx.x / (kRowsWG / 4);
+  const int rloc = (blockIdx.x % (kRowsWG / 4)) * 4 + threadIdx.x / TPR;
   const int t = threadIdx.x % TPR;
+  const int sg = blockIdx.y, s = sg / a.hkv, g = sg % a.hkv;
+  const int rt = ctile < ctiles_full ? ctile : a.rt_full;
+  const int splits = rt < a.rt_full ? a.s_full : a.s_part;
   const int n = a.n_nodes[s];
   const int P = a.prefix_len[s];
   if (!seq_ok(n, P, a.max_nodes, a.max_pages, a.err, false)) return;
+  const int r = rt * kRowsWG + rloc;
   if (r >= n * a.group) return;
   const int node = r / a.group, hq = g * a.group + r % a.group;
-  const size_t base = (static_cast<size_t>(s) * a.hkv + g) * a.splits;
+  const size_t gbase = static_cast<size_t>(sg) * a.part_rows_group;
   float M = -INFINITY;
-  for (int sp = 0; sp < a.splits; ++sp) M = fmaxf(M, a.part_lse[(base + sp) * a.rows_pad + r]);
+  for (int sp = 0; sp < splits; ++sp)
+    M = fmaxf(M, a.part_lse[gbase + part_row(a, rt, sp) + rloc]);
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
   float wsum = 0.0f;
-  for (int sp = 0; sp < a.splits; ++sp) {
-    const size_t prow = (base + sp) * a.rows_pad + r;
+  for (int sp = 0; sp < splits; ++sp) {
+    const size_t prow = gbase + part_row(a, rt, sp) + rloc;
     const float ls = a.part_lse[prow];
     if (ls == -INFINITY) continue;
     const float wgt = expf(ls - M);
@@ -458,22 +515,41 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32(
 // ------------------------------------------------------------------ host side
 
 struct AttnPlan {
-  int row_tiles, rows_pad, splits;
+  int rt_full, has_partial, s_full, s_part, ngroups, slots_per_xcd, ctiles;
+  int part_rows_group, full_part_rows;
   size_t off_lse, bytes;
 };
 
 static AttnPlan attn_plan(const AttnShape& s) {
   AttnPlan p{};
   const int group = s.hq / s.hkv;
-  p.row_tiles = (s.max_nodes * group + kRowsWG - 1) / kRowsWG;
-  p.rows_pad = p.row_tiles * kRowsWG;
-  const long long base = static_cast<long long>(p.row_tiles) * s.hkv * s.batch;
+  const int rmax = s.max_nodes * group;
+  p.rt_full = rmax / kRowsWG;
+  p.has_partial = (rmax % kRowsWG) != 0;
+  p.ngroups = s.batch * s.hkv;
   const int tiles = (s.max_pages * s.page_size + kKT - 1) / kKT;
-  const long long want = (512 + base - 1) / std::max<long long>(1, base);
-  p.splits = static_cast<int>(std::max<long long>(1, std::min<long long>(want, std::min(tiles, 32))));
-  if (s.dt == JT_F32) p.splits = 1;
-  if (p.splits > 1) {
-    const size_t rows = static_cast<size_t>(s.batch) * s.hkv * p.splits * p.rows_pad;
+  const int min_splits = (tiles + kMaxTilesItem - 1) / kMaxTilesItem;  // page list fits LDS
+  // full tiles: enough items to fill 256 CUs once
+  const long long full_items = static_cast<long long>(p.ngroups) * p.rt_full;
+  int sf = full_items > 0 ? static_cast<int>((256 + full_items - 1) / full_items) : 1;
+  if (full_items >= 192) sf = 1;
+  p.s_full = std::max(min_splits, std::min(sf, std::max(1, tiles)));
+  // the partial tile has few rows: split it finely so it trails the full tiles
+  int sp = static_cast<int>((256 + p.ngroups - 1) / std::max(1, p.ngroups));
+  sp = std::max(sp, 4);
+  p.s_part = p.has_partial ? std::max(min_splits, std::min(sp, std::max(1, tiles))) : 0;
+  const int items = p.rt_full * p.s_full + p.has_partial * p.s_part;
+  const int gx_max = (p.ngroups + kXcds - 1) / kXcds;
+  p.slots_per_xcd = gx_max * items;
+  p.full_part_rows = p.s_full > 1 ? p.rt_full * p.s_full * kRowsWG : 0;
+  p.part_rows_group = p.full_part_rows + ((p.has_partial && p.s_part > 1) ? p.s_part * kRowsWG : 0);
+  p.ctiles = (p.s_full > 1 ? p.rt_full : 0) + ((p.has_partial && p.s_part > 1) ? 1 : 0);
+  if (s.dt == JT_F32) {
+    p.part_rows_group = 0;
+    p.ctiles = 0;
+  }
+  if (p.part_rows_group > 0) {
+    const size_t rows = static_cast<size_t>(p.ngroups) * p.part_rows_group;
     p.off_lse = (rows * s.head_dim * sizeof(float) + 255) / 256 * 256;
     p.bytes = p.off_lse + (rows * sizeof(float) + 255) / 256 * 256;
   }
@@ -488,12 +564,12 @@ size_t tree_attention_workspace_bytes(const AttnShape& s) {
 template <int D>
 static hipError_t launch_mfma(const AttnShape& sh, const AttnPlan& p, AttnArgs& a,
                               hipStream_t stream) {
-  hipLaunchKernelGGL(tree_attn_mfma<D>, dim3(p.row_tiles * p.splits, sh.hkv, sh.batch),
-                     dim3(kAttnThreads), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.splits == 1) return e;
-  hipLaunchKernelGGL(tree_attn_combine<D>, dim3(p.rows_pad / 4, sh.hkv, sh.batch), dim3(256), 0,
+  hipLaunchKernelGGL(tree_attn_mfma<D>, dim3(kXcds * p.slots_per_xcd), dim3(kAttnThreads), 0,
                      stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || p.ctiles == 0) return e;
+  hipLaunchKernelGGL(tree_attn_combine<D>, dim3(p.ctiles * (kRowsWG / 4), p.ngroups), dim3(256),
+                     0, stream, a);
   return hipGetLastError();
 }
 
@@ -525,8 +601,8 @@ hipError_t tree_attention_launch(const AttnShape& sh, const void* q, const void*
   a.anc = anc_mask;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.part_o = p.splits > 1 ? static_cast<float*>(workspace) : nullptr;
-  a.part_lse = p.splits > 1
+  a.part_o = p.part_rows_group > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.part_lse = p.part_rows_group > 0
                    ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + p.off_lse)
                    : nullptr;
   a.err = err;
@@ -536,10 +612,16 @@ hipError_t tree_attention_launch(const AttnShape& sh, const void* q, const void*
   a.group = sh.hq / sh.hkv;
   a.max_pages = sh.max_pages;
   a.num_pages = sh.num_pages;
-  a.splits = p.splits;
-  a.row_tiles = p.row_tiles;
-  a.rows_pad = p.rows_pad;
   a.nwords = nwords;
+  a.rt_full = p.rt_full;
+  a.s_full = p.s_full;
+  a.s_part = p.s_part;
+  a.has_partial = p.has_partial;
+  a.items_full = p.rt_full * p.s_full;
+  a.items_part = p.has_partial * p.s_part;
+  a.ngroups = p.ngroups;
+  a.part_rows_group = p.part_rows_group;
+  a.full_part_rows = p.full_part_rows;
   a.scale_log2 = scale * kLog2e;
   if (sh.head_dim == 64) return launch_mfma<64>(sh, p, a, stream);
   return launch_mfma<128>(sh, p, a, stream);
