@@ -396,3 +396,15 @@ def test_accept_bf16_logits():
         L, nodes, bb = O.accept(Xf[s].numpy(), p, tok, d, T, 4)
         assert (alen[s], bonus[s]) == (L, bb) and np.array_equal(anodes[s], nodes)
     assert alen[0] == 4
+
+
+@pytest.mark.parametrize("N,W,Bb", [(24, 2, 100), (40, 1, 60), (17, 3, 200)])
+def test_build_tree_deep(N, W, Bb):
+    """Depths past 16 take the kernel variant sized for up to 64 levels."""
+    rng = np.random.default_rng(N * 100 + W)
+    L = (rng.standard_normal((2, N, 500)) * rng.uniform(1, 10)).astype(np.float32)
+    roots = np.array([3, 4], dtype=np.int32)
+    g = _gpu_build(torch.from_numpy(L), W, Bb, torch.from_numpy(roots))
+    for s in range(2):
+        ref = O.build_tree(L[s], W, Bb, int(roots[s]), check_exact=False)
+        _assert_tree_equal(g, ref, s, f"deep N={N}")

@@ -39,25 +39,41 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax(
   bool bad = false;
   if (VEC > 1) {
     // begin and end are multiples of VEC here (host guarantees vocab % VEC == 0
-    // and chunk_len % VEC == 0), and rows start VEC-aligned.
-    for (int i = begin + threadIdx.x * VEC; i < end; i += kArgmaxThreads * VEC) {
-      float v[VEC];
-      if constexpr (sizeof(T) == 4) {
-        const float4 f = *reinterpret_cast<const float4*>(x + i);
-        v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
-      } else {
-        const uint4 u = *reinterpret_cast<const uint4*>(x + i);
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+    // and chunk_len % VEC == 0), and rows start VEC-aligned.  UNR loads per
+    // thread are issued before any of them is consumed.
+    constexpr int UNR = 4;
+    for (int i0 = begin + threadIdx.x * VEC; i0 < end; i0 += kArgmaxThreads * VEC * UNR) {
+      float v[UNR][VEC];
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          v[2 * k] = __uint_as_float(w[k] << 16);
-          v[2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+      for (int u = 0; u < UNR; ++u) {
+        const int i = i0 + u * kArgmaxThreads * VEC;
+        if (i < end) {
+          if constexpr (sizeof(T) == 4) {
+            const float4 f = *reinterpret_cast<const float4*>(x + i);
+            v[u][0] = f.x; v[u][1] = f.y; v[u][2] = f.z; v[u][3] = f.w;
+          } else {
+            const uint4 q = *reinterpret_cast<const uint4*>(x + i);
+            const uint32_t w[4] = {q.x, q.y, q.z, q.w};
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              v[u][2 * k] = __uint_as_float(w[k] << 16);
+              v[u][2 * k + 1] = __uint_as_float(w[k] & 0xFFFF0000u);
+            }
+          }
+        } else {
+#pragma unroll
+          for (int k = 0; k < VEC; ++k) v[u][k] = -INFINITY;
         }
       }
 #pragma unroll
-      for (int k = 0; k < VEC; ++k) {
-        if (v[k] != v[k]) { bad = true; continue; }
-        if (better(v[k], i + k, bv, bi)) { bv = v[k]; bi = i + k; }
+      for (int u = 0; u < UNR; ++u) {
+        const int i = i0 + u * kArgmaxThreads * VEC;
+#pragma unroll
+        for (int k = 0; k < VEC; ++k) {
+          const float y = v[u][k];
+          if (y != y) { bad = true; continue; }
+          if (i + k < end && better(y, i + k, bv, bi)) { bv = y; bi = i + k; }
+        }
       }
     }
   } else {

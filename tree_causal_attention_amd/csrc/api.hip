@@ -48,7 +48,8 @@ jt_status jt_build_tree(const void* draft_logits, jt_dtype dt, int batch, int de
   if (batch < 0 || depth_n < 1 || vocab < 1 || width_w < 1 || budget_b < 0 || !valid_dtype(dt))
     return JT_ERR_INVALID_ARG;
   if (width_w > vocab) return JT_ERR_INVALID_ARG;
-  if (depth_n > kMaxDepth || width_w > kMaxWidth || budget_b + 1 > kMaxNodes)
+  if (depth_n > kMaxDepth || width_w > kMaxWidth || budget_b + 1 > kMaxNodes ||
+      vocab > jt::build_tree_max_vocab())
     return JT_ERR_UNSUPPORTED;
   if (jt::build_tree_lds_bytes(depth_n, width_w, budget_b) > kMaxSelectLds)
     return JT_ERR_UNSUPPORTED;

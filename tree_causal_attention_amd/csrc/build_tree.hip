@@ -4,9 +4,10 @@
 // Method: JetSpec news piece (mlqm.cn/news/158889), tree-construction
 // paragraph; JetSpec explainer (techwalker.com, "加速AI思考…"), section 五.
 //
-// draft_row_scan: one workgroup per (row chunk, depth row); streams the fp32
-//   logits once, keeping a running (max, fp64 sum of exp) and a per-thread
-//   sorted top-W list, then reduces them over the workgroup.  HBM-bound.
+// draft_row_scan: one workgroup per (vocab chunk, depth row); reads the logits
+//   with 16-byte loads, finds the chunk max and per-thread sorted top-W lists,
+//   then sums exp(x - max) in fp64 over the (L2-resident) chunk and merges the
+//   lists over the workgroup.
 // tree_select: one workgroup per sequence.  The best-first pop order equals
 //   the B smallest keys (-score, parent index, rank) of the complete tree,
 //   because a child never precedes its parent.  It is computed level by level:
@@ -28,77 +29,175 @@ namespace jt {
 constexpr int kScanThreads = 256;
 constexpr int kSelectThreads = 1024;
 
-template <typename T, int WMAX>
+template <typename T, int VEC>
+__device__ __forceinline__ void load_vec(const T* x, int i, float (&v)[VEC]) {
+  if constexpr (VEC == 1) {
+    v[0] = load_as_f32(x, i);
+  } else if constexpr (sizeof(T) == 4) {
+    const float4 f = *reinterpret_cast<const float4*>(x + i);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + i);
+    const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(wds[k] << 16);
+      v[2 * k + 1] = __uint_as_float(wds[k] & 0xFFFF0000u);
+    }
+  }
+}
+
+constexpr int kCandCap = 1024;  // threshold candidates kept per chunk
+
+// One workgroup per (vocab chunk, depth row); thread t holds EPT logits of
+// the chunk in registers (16-byte loads, one pass over HBM).
+//  * max and the fp64 sum of exp(x - max) come straight from the registers;
+//  * top-W: the W-th largest per-thread maximum L is a lower bound of the
+//    chunk's W-th largest logit (W distinct threads hold a value >= L), so
+//    only logits >= L are collected in LDS and ranked; if more than kCandCap
+//    qualify (e.g. massive ties) every thread builds its exact sorted top-W and
+//    W rounds of "best head" merge them.
+template <typename T, int WMAX, int VEC, int EPT>
 __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
     const T* __restrict__ logits, int vocab, int chunks, int chunk_len, int width,
     float* __restrict__ part_max, double* __restrict__ part_sum, float* __restrict__ part_val,
     int* __restrict__ part_idx, int32_t* err) {
-  const int row = blockIdx.y, c = blockIdx.x;
+  constexpr int NV = EPT / VEC;
+  __shared__ float sm_m[kScanThreads / kWave];
+  __shared__ double sm_s[kScanThreads / kWave];
+  __shared__ float sm_tmax[kScanThreads];
+  __shared__ float sm_cv[kCandCap];
+  __shared__ int sm_ci[kCandCap];
+  __shared__ int sm_n;
+  __shared__ float sm_L;
+  __shared__ float sm_v[kScanThreads / kWave];
+  __shared__ int sm_i[kScanThreads / kWave];
+
+  const int row = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
+  const int lane = t % kWave, wv = t / kWave;
   const int begin = c * chunk_len;
   const int end = min(vocab, begin + chunk_len);
   const T* x = logits + static_cast<size_t>(row) * vocab;
 
-  float m = -INFINITY;
-  double s = 0.0;
+  float xv[EPT];
   bool bad = false;
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = begin + (j * kScanThreads + t) * VEC;
+    float v[VEC];
+    if (i < end) {
+      load_vec<T, VEC>(x, i, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] = -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float y = v[e];
+      if (y != y || y == INFINITY) { bad = true; y = -INFINITY; }
+      xv[j * VEC + e] = y;
+      m = fmaxf(m, y);
+    }
+  }
+  if (bad) report(err, JT_DERR_BAD_LOGIT);
+  if (t == 0) sm_n = 0;
+
+  // ---- chunk max
+  float wm = m;
+  for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, shfl_xor(wm, o));
+  if (lane == 0) sm_m[wv] = wm;
+  sm_tmax[t] = m;
+  __syncthreads();
+  float M = sm_m[0];
+  for (int w = 1; w < kScanThreads / kWave; ++w) M = fmaxf(M, sm_m[w]);
+
+  // ---- fp64 sum of exp(x - M) over the registers
+  double sacc = 0.0;
+  if (M != -INFINITY) {
+    const double Md = static_cast<double>(M);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const double e = exp(static_cast<double>(fmaxf(xv[k], -1.0e30f)) - Md);
+      sacc += (xv[k] != -INFINITY) ? e : 0.0;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) sacc += shfl_xor_f64(sacc, o);
+  if (lane == 0) sm_s[wv] = sacc;
+
+  // ---- threshold: the W-th largest thread maximum (ties by thread id)
+  int rank = 0;
+  for (int u = 0; u < kScanThreads; ++u) {
+    const float mu = sm_tmax[u];
+    rank += (mu > m || (mu == m && u < t)) ? 1 : 0;
+  }
+  if (rank == width - 1) sm_L = m;
+  __syncthreads();
+  if (t == 0) {
+    double S = 0.0;
+    for (int w = 0; w < kScanThreads / kWave; ++w) S += sm_s[w];
+    part_max[row * chunks + c] = M;
+    part_sum[row * chunks + c] = S;
+  }
+  const float L = sm_L;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = begin + (j * kScanThreads + t) * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (i + e < end && xv[j * VEC + e] >= L) {
+        const int pos = atomicAdd(&sm_n, 1);
+        if (pos < kCandCap) { sm_cv[pos] = xv[j * VEC + e]; sm_ci[pos] = i + e; }
+      }
+    }
+  }
+  __syncthreads();
+  const int nc = sm_n;
+  const size_t out0 = (static_cast<size_t>(row) * chunks + c) * width;
+  if (nc <= kCandCap) {
+    for (int q = t; q < nc; q += kScanThreads) {
+      const float vq = sm_cv[q];
+      const int iq = sm_ci[q];
+      int r = 0;
+      for (int u = 0; u < nc; ++u) r += better(sm_cv[u], sm_ci[u], vq, iq) ? 1 : 0;
+      if (r < width) { part_val[out0 + r] = vq; part_idx[out0 + r] = iq; }
+    }
+    for (int r = nc + t; r < width; r += kScanThreads) {
+      part_val[out0 + r] = -INFINITY;
+      part_idx[out0 + r] = INT32_MAX;
+    }
+    return;
+  }
+
+  // ---- overflow: exact per-thread sorted lists, merged by W rounds
   float tv[WMAX];
   int ti[WMAX];
 #pragma unroll
   for (int k = 0; k < WMAX; ++k) { tv[k] = -INFINITY; ti[k] = INT32_MAX; }
-
-  for (int i = begin + threadIdx.x; i < end; i += kScanThreads) {
-    const float v = load_as_f32(x, i);
-    if (v != v || v == INFINITY) { bad = true; continue; }
-    if (v != -INFINITY) {
-      if (v > m) {
-        s = s * exp(static_cast<double>(m) - static_cast<double>(v)) + 1.0;
-        m = v;
-      } else {
-        s += exp(static_cast<double>(v) - static_cast<double>(m));
-      }
-    }
-    if (better(v, i, tv[WMAX - 1], ti[WMAX - 1])) {
-      // Sorted insert as a select network: slot k keeps its entry if it
-      // precedes the new one, takes the new one at the first slot it beats,
-      // and takes its predecessor's entry after that.  Slots are rewritten
-      // from the last one up, so slot k-1 still holds its old entry.
 #pragma unroll
-      for (int k = WMAX - 1; k >= 0; --k) {
-        const int u = k > 0 ? k - 1 : 0;
-        const bool b = better(v, i, tv[k], ti[k]);
-        const bool b_up = k > 0 && better(v, i, tv[u], ti[u]);
-        const float up_v = tv[u];
-        const int up_i = ti[u];
-        tv[k] = b ? (b_up ? up_v : v) : tv[k];
-        ti[k] = b ? (b_up ? up_i : i) : ti[k];
+  for (int j = 0; j < NV; ++j) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int i = begin + (j * kScanThreads + t) * VEC + e;
+      const float y = xv[j * VEC + e];
+      if (i < end && better(y, i, tv[WMAX - 1], ti[WMAX - 1])) {
+        // Sorted insert as a select network: slot k keeps its entry if it
+        // precedes the new one, takes the new one at the first slot it beats,
+        // and takes its predecessor's entry after that.  Slots are rewritten
+        // from the last one up, so slot k-1 still holds its old entry.
+#pragma unroll
+        for (int k = WMAX - 1; k >= 0; --k) {
+          const int u = k > 0 ? k - 1 : 0;
+          const bool b = better(y, i, tv[k], ti[k]);
+          const bool b_up = k > 0 && better(y, i, tv[u], ti[u]);
+          const float up_v = tv[u];
+          const int up_i = ti[u];
+          tv[k] = b ? (b_up ? up_v : y) : tv[k];
+          ti[k] = b ? (b_up ? up_i : i) : ti[k];
+        }
       }
     }
   }
-  if (bad) report(err, JT_DERR_BAD_LOGIT);
-
-  // ---- (max, sum) over the workgroup
-  __shared__ float sm_m[kScanThreads / kWave];
-  __shared__ double sm_s[kScanThreads / kWave];
-  __shared__ float sm_v[kScanThreads / kWave];
-  __shared__ int sm_i[kScanThreads / kWave];
-  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-  float wm = m;
-  for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, shfl_xor(wm, o));
-  double ws = (m == -INFINITY) ? 0.0 : s * exp(static_cast<double>(m) - static_cast<double>(wm));
-  for (int o = 32; o > 0; o >>= 1) ws += shfl_xor_f64(ws, o);
-  if (lane == 0) { sm_m[wv] = wm; sm_s[wv] = ws; }
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    float M = -INFINITY;
-    for (int w = 0; w < kScanThreads / kWave; ++w) M = fmaxf(M, sm_m[w]);
-    double S = 0.0;
-    for (int w = 0; w < kScanThreads / kWave; ++w)
-      if (sm_m[w] != -INFINITY) S += sm_s[w] * exp(static_cast<double>(sm_m[w]) - static_cast<double>(M));
-    part_max[row * chunks + c] = M;
-    part_sum[row * chunks + c] = S;
-  }
-
-  // ---- top-W over the workgroup: W rounds of (best head, pop it)
   for (int r = 0; r < width; ++r) {
     float bv = tv[0];
     int bi = ti[0];
@@ -114,10 +213,7 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
     int gi = sm_i[0];
     for (int w = 1; w < kScanThreads / kWave; ++w)
       if (better(sm_v[w], sm_i[w], gv, gi)) { gv = sm_v[w]; gi = sm_i[w]; }
-    if (threadIdx.x == 0) {
-      part_val[(static_cast<size_t>(row) * chunks + c) * width + r] = gv;
-      part_idx[(static_cast<size_t>(row) * chunks + c) * width + r] = gi;
-    }
+    if (t == 0) { part_val[out0 + r] = gv; part_idx[out0 + r] = gi; }
     if (ti[0] == gi && gi != INT32_MAX) {
 #pragma unroll
       for (int k = 0; k + 1 < WMAX; ++k) { tv[k] = tv[k + 1]; ti[k] = ti[k + 1]; }
@@ -140,6 +236,7 @@ __host__ __device__ inline int level_cap(int d, int width, int budget) {
 struct SelectLayout {
   int tot;         // sum of level capacities
   int capmax;      // max level capacity
+  int top;         // power of two >= capmax (binary-lifting start)
   size_t off_S, off_lse, off_cval, off_ctok, off_loff, off_lcnt, off_rawa, off_rawb;
   size_t off_score, off_info, off_gidx, bytes;
 };
@@ -153,6 +250,8 @@ inline SelectLayout select_layout(int depth_n, int width, int budget, int wmax) 
     L.tot += c;
     L.capmax = std::max(L.capmax, c);
   }
+  L.top = 1;
+  while (L.top < L.capmax) L.top <<= 1;
   size_t o = 0;
   auto take = [&](size_t n, size_t align) { o = (o + align - 1) / align * align; size_t r = o; o += n; return r; };
   L.off_S = take(sizeof(double) * (depth_n + 1), 8);
@@ -170,40 +269,28 @@ inline SelectLayout select_layout(int depth_n, int width, int budget, int wmax) 
   return L;
 }
 
-// Number of candidates (p', k2) of the level being built that precede the
-// candidate with score s and parent position p: the predicate is true on a
-// prefix of p' because column k2 is sorted by score.
-__device__ __forceinline__ int count_before(const double* raw_prev, int m, double vk2, double Sd,
-                                            double s, int p, bool inclusive) {
-  int lo = 0, hi = m;
-  while (lo < hi) {
-    const int mid = (lo + hi) >> 1;
-    const double sc = (raw_prev[mid] + vk2) - Sd;
-    const bool pred = sc > s || (sc == s && (inclusive ? mid <= p : mid < p));
-    if (pred) lo = mid + 1; else hi = mid;
-  }
-  return lo;
-}
-
-// Does kept node (d2, j) precede kept node (d, i), d2 != d?  Scores first;
-// exact ties compare the parents' keys, walking up both paths (their depths
-// keep differing, so they never meet; the root precedes every other node).
-__device__ __forceinline__ bool precedes_cross(const double* score, const uint32_t* info,
-                                               const int* loff, int d2, int j, int d, int i) {
+// Does kept node (d2, j) precede kept node (d, i), d2 != d, given that their
+// scores are equal?  Compare the parents' keys, walking up both paths (their
+// depths keep differing, so they never meet; the root precedes every node).
+__device__ __noinline__ bool precedes_tied(const double* score, const uint32_t* info,
+                                           const int* loff, int d2, int j, int d, int i) {
   while (true) {
-    const double sy = score[loff[d2] + j];
-    const double sx = score[loff[d] + i];
-    if (sy != sx) return sy > sx;
     j = static_cast<int>(info[loff[d2] + j] & 0xFFFFu);
     i = static_cast<int>(info[loff[d] + i] & 0xFFFFu);
     --d2;
     --d;
     if (d2 == 0) return true;
     if (d == 0) return false;
+    const double sy = score[loff[d2] + j];
+    const double sx = score[loff[d] + i];
+    if (sy != sx) return sy > sx;
   }
 }
 
-template <int WMAX>
+// Binary lifting over a prefix-true predicate runs a fixed number of steps
+// (top = a power of two >= every list length), so the W - 1 (or N - 1)
+// searches of one candidate advance in lockstep and their LDS reads overlap.
+template <int WMAX, int NMAX>
 __global__ __launch_bounds__(kSelectThreads) void tree_select(
     const float* __restrict__ part_max, const double* __restrict__ part_sum,
     const float* __restrict__ part_val, const int* __restrict__ part_idx, int chunks, int depth_n,
@@ -226,13 +313,23 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   const int seq = blockIdx.x;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int nwaves = kSelectThreads / kWave;
+  const int top = L.top;
 
-  // ---- phase 1: merge the chunk partials of every depth (one wave a depth)
+  // ---- phase 1: merge the chunk partials of every depth (one wave a depth);
+  // each lane holds one chunk's sorted candidates in registers.
   for (int d = wv; d < depth_n; d += nwaves) {
     const size_t row = static_cast<size_t>(seq) * depth_n + d;
     const bool act = lane < chunks;
     const float mc = act ? part_max[row * chunks + lane] : -INFINITY;
     const double sc = act ? part_sum[row * chunks + lane] : 0.0;
+    float hv[WMAX];
+    int hid[WMAX];
+#pragma unroll
+    for (int k = 0; k < WMAX; ++k) {
+      const bool ok = act && k < width;
+      hv[k] = ok ? part_val[(row * chunks + lane) * width + k] : -INFINITY;
+      hid[k] = ok ? part_idx[(row * chunks + lane) * width + k] : INT32_MAX;
+    }
     float M = mc;
     for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
     double contrib = (mc == -INFINITY) ? 0.0 : sc * exp(static_cast<double>(mc) - static_cast<double>(M));
@@ -245,22 +342,20 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
         lse[d] = static_cast<double>(M) + log(contrib);
       }
     }
-    int ptr = 0;
     for (int r = 0; r < width; ++r) {
-      float hv = -INFINITY;
-      int hi = INT32_MAX;
-      if (act && ptr < width) {
-        hv = part_val[(row * chunks + lane) * width + ptr];
-        hi = part_idx[(row * chunks + lane) * width + ptr];
-      }
-      float bv = hv;
-      int bi = hi;
+      float bv = hv[0];
+      int bi = hid[0];
       for (int o = 32; o > 0; o >>= 1) {
         const float ov = shfl_xor(bv, o);
         const int oi = shfl_xor(bi, o);
         if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
       }
-      if (act && ptr < width && hi == bi) ++ptr;
+      if (hid[0] == bi && bi != INT32_MAX) {  // this lane's head won: pop it
+#pragma unroll
+        for (int k = 0; k + 1 < WMAX; ++k) { hv[k] = hv[k + 1]; hid[k] = hid[k + 1]; }
+        hv[WMAX - 1] = -INFINITY;
+        hid[WMAX - 1] = INT32_MAX;
+      }
       if (lane == 0) { cval[d * WMAX + r] = bv; ctok[d * WMAX + r] = bi; }
     }
   }
@@ -286,22 +381,38 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
     const int cap = level_cap(d, width, budget);
     if (cap <= 0 || m_prev == 0) break;
     const double Sd = S[d];
+    double cv[WMAX];
+#pragma unroll
+    for (int k = 0; k < WMAX; ++k) cv[k] = static_cast<double>(cval[(d - 1) * WMAX + (k < width ? k : 0)]);
     const int ncand = m_prev * width;
     for (int idx = tid; idx < ncand; idx += kSelectThreads) {
       const int k = idx / m_prev, p = idx % m_prev;
       if ((p + 1) * (k + 1) > cap) continue;
-      const double vk = static_cast<double>(cval[(d - 1) * WMAX + k]);
+      double vk = cv[0];
+#pragma unroll
+      for (int kk = 1; kk < WMAX; ++kk) vk = (kk == k) ? cv[kk] : vk;
       const double raw = raw_prev[p] + vk;
-      const double s = raw - Sd;
-      int r = p;
-      for (int k2 = 0; k2 < width; ++k2) {
-        if (k2 == k) continue;
-        r += count_before(raw_prev, m_prev, static_cast<double>(cval[(d - 1) * WMAX + k2]), Sd, s, p,
-                          k2 < k);
-        if (r >= cap) break;
+      const double sc = raw - Sd;
+      int cnt[WMAX];
+#pragma unroll
+      for (int k2 = 0; k2 < WMAX; ++k2) cnt[k2] = 0;
+      for (int sz = top; sz > 0; sz >>= 1) {
+        // branch-free step: every column's read is issued before any compare
+#pragma unroll
+        for (int k2 = 0; k2 < WMAX; ++k2) {
+          const int mid = cnt[k2] + sz;
+          const int q = min(mid, m_prev) - 1;
+          const double s2 = (raw_prev[q] + cv[k2]) - Sd;
+          const bool pred = k2 < width && k2 != k && mid <= m_prev &&
+                            (s2 > sc || (s2 == sc && (k2 < k ? q <= p : q < p)));
+          cnt[k2] = pred ? mid : cnt[k2];
+        }
       }
+      int r = p;
+#pragma unroll
+      for (int k2 = 0; k2 < WMAX; ++k2) r += cnt[k2];
       if (r < cap) {
-        lv_score[loff[d] + r] = s;
+        lv_score[loff[d] + r] = sc;
         lv_info[loff[d] + r] = static_cast<uint32_t>(p) | (static_cast<uint32_t>(k) << 16);
         raw_cur[r] = raw;
       }
@@ -317,25 +428,49 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
     for (int d = last_level + 1; d <= depth_n; ++d) lcnt[d] = 0;
   __syncthreads();
 
-  // ---- phase 3: global rank of every kept node
+  // ---- phase 3: global rank of every kept node (lockstep searches over levels)
+  int lo_r[NMAX], lc_r[NMAX];
   int total = 0;
-  for (int d = 1; d <= depth_n; ++d) total += lcnt[d];
+#pragma unroll
+  for (int d2 = 0; d2 < NMAX; ++d2) {
+    lo_r[d2] = (d2 + 1 <= depth_n) ? loff[d2 + 1] : 0;
+    lc_r[d2] = (d2 + 1 <= depth_n) ? lcnt[d2 + 1] : 0;
+    total += lc_r[d2];
+  }
   const int n_sel = min(budget, total);
   for (int idx = tid; idx < loff[depth_n + 1]; idx += kSelectThreads) {
     int d = 1;
     while (idx >= loff[d + 1]) ++d;
     const int i = idx - loff[d];
     if (i >= lcnt[d]) continue;
-    int R = i;
-    for (int d2 = 1; d2 <= depth_n && R < budget; ++d2) {
-      if (d2 == d || lcnt[d2] == 0) continue;
-      int lo = 0, hi = lcnt[d2];
-      while (lo < hi) {
-        const int mid = (lo + hi) >> 1;
-        if (precedes_cross(lv_score, lv_info, loff, d2, mid, d, i)) lo = mid + 1; else hi = mid;
+    const double sx = lv_score[idx];
+    int cnt[NMAX];
+#pragma unroll
+    for (int d2 = 0; d2 < NMAX; ++d2) cnt[d2] = 0;
+    for (int sz = top; sz > 0; sz >>= 1) {
+      // fast path branch-free; exact cross-level score ties (rare) resolved after
+      bool tie[NMAX];
+      bool any_tie = false;
+#pragma unroll
+      for (int d2 = 0; d2 < NMAX; ++d2) {
+        const int mid = cnt[d2] + sz;
+        const bool ok = d2 + 1 != d && mid <= lc_r[d2];
+        const int q = max(0, min(mid, lc_r[d2]) - 1);
+        const double sy = lv_score[lo_r[d2] + q];
+        tie[d2] = ok && sy == sx;
+        any_tie |= tie[d2];
+        cnt[d2] = (ok && sy > sx) ? mid : cnt[d2];
       }
-      R += lo;
+      if (any_tie) {
+#pragma unroll
+        for (int d2 = 0; d2 < NMAX; ++d2)
+          if (tie[d2] && precedes_tied(lv_score, lv_info, loff, d2 + 1, cnt[d2] + sz - 1, d, i))
+            cnt[d2] += sz;
+      }
     }
+    int R = i;
+#pragma unroll
+    for (int d2 = 0; d2 < NMAX; ++d2) R += cnt[d2];
     lv_gidx[idx] = (R < budget) ? static_cast<uint16_t>(R + 1) : static_cast<uint16_t>(0xFFFF);
   }
   __syncthreads();
@@ -374,18 +509,23 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
 // ------------------------------------------------------------------ host side
 
 struct ScanPlan {
-  int rows, chunks, chunk_len, wmax;
+  int rows, chunks, chunk_len, wmax, vec, ept;
 };
 
-static ScanPlan scan_plan(int batch, int depth_n, int vocab, int width) {
+static int wmax_of(int width) {
+  return width <= 1 ? 1 : width <= 2 ? 2 : width <= 4 ? 4 : width <= 8 ? 8 : 16;
+}
+
+// A chunk is 256 threads x EPT logits (EPT = 32, or 128 for vocabularies
+// past 512K); at most 64 chunks per row (tree_select merges one per lane).
+static ScanPlan scan_plan(int batch, int depth_n, int vocab, int width, int vec) {
   ScanPlan p{};
   p.rows = batch * depth_n;
-  const int by_rows = std::max(1, (1024 + p.rows - 1) / std::max(1, p.rows));
-  const int by_vocab = std::max(1, (vocab + 2047) / 2048);
-  p.chunks = std::min(64, std::min(by_rows, by_vocab));
-  p.chunk_len = (vocab + p.chunks - 1) / p.chunks;
+  p.vec = vec;
+  p.ept = (vocab <= 64 * kScanThreads * 32) ? 32 : 128;
+  p.chunk_len = kScanThreads * p.ept;
   p.chunks = (vocab + p.chunk_len - 1) / p.chunk_len;
-  p.wmax = width <= 1 ? 1 : width <= 2 ? 2 : width <= 4 ? 4 : width <= 8 ? 8 : 16;
+  p.wmax = wmax_of(width);
   return p;
 }
 
@@ -406,71 +546,93 @@ static ScanWorkspace scan_workspace(const ScanPlan& p, int width) {
   return w;
 }
 
+int build_tree_max_vocab() { return 64 * kScanThreads * 128; }
+
 size_t build_tree_workspace_bytes(int batch, int depth_n, int vocab, int width) {
   if (batch <= 0) return 0;
-  return scan_workspace(scan_plan(batch, depth_n, vocab, width), width).bytes;
+  // vec 1 gives the most chunks of the possible plans
+  return scan_workspace(scan_plan(batch, depth_n, vocab, width, 1), width).bytes;
 }
 
 size_t build_tree_lds_bytes(int depth_n, int width, int budget) {
-  const ScanPlan p = scan_plan(1, depth_n, std::max(width, 1), width);
-  return select_layout(depth_n, width, budget, p.wmax).bytes;
+  return select_layout(depth_n, width, budget, wmax_of(width)).bytes;
+}
+
+template <typename T, int WMAX, int VEC>
+static void launch_scan(const void* logits, int vocab, int width, const ScanPlan& p, float* pm,
+                        double* ps, float* pv, int* pi, int32_t* err, hipStream_t stream) {
+  if (p.ept == 32)
+    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 32>), dim3(p.chunks, p.rows),
+                       dim3(kScanThreads), 0, stream, static_cast<const T*>(logits), vocab,
+                       p.chunks, p.chunk_len, width, pm, ps, pv, pi, err);
+  else
+    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 128>), dim3(p.chunks, p.rows),
+                       dim3(kScanThreads), 0, stream, static_cast<const T*>(logits), vocab,
+                       p.chunks, p.chunk_len, width, pm, ps, pv, pi, err);
 }
 
 template <typename T, int WMAX>
-static hipError_t launch_build(const void* logits, int batch, int depth_n, int vocab, int width,
-                               int budget, const ScanPlan& p, const ScanWorkspace& w,
-                               unsigned char* ws, const int32_t* root_token, int32_t* parent,
-                               int32_t* token, int32_t* depth, double* score, int32_t* n_nodes,
-                               int32_t* err, hipStream_t stream) {
-  float* part_max = reinterpret_cast<float*>(ws + w.off_max);
-  double* part_sum = reinterpret_cast<double*>(ws + w.off_sum);
-  float* part_val = reinterpret_cast<float*>(ws + w.off_val);
-  int* part_idx = reinterpret_cast<int*>(ws + w.off_idx);
-  hipLaunchKernelGGL((draft_row_scan<T, WMAX>), dim3(p.chunks, p.rows), dim3(kScanThreads), 0,
-                     stream, static_cast<const T*>(logits), vocab, p.chunks, p.chunk_len, width,
-                     part_max, part_sum, part_val, part_idx, err);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  const SelectLayout L = select_layout(depth_n, width, budget, WMAX);
-  hipLaunchKernelGGL((tree_select<WMAX>), dim3(batch), dim3(kSelectThreads), L.bytes, stream,
-                     part_max, part_sum, part_val, part_idx, p.chunks, depth_n, width, budget, L,
-                     root_token, parent, token, depth, score, n_nodes, err);
-  return hipGetLastError();
+static void scan_vec(const void* logits, int vocab, int width, const ScanPlan& p, float* pm,
+                     double* ps, float* pv, int* pi, int32_t* err, hipStream_t stream) {
+  constexpr int V = sizeof(T) == 4 ? 4 : 8;
+  if (p.vec == V) launch_scan<T, WMAX, V>(logits, vocab, width, p, pm, ps, pv, pi, err, stream);
+  else launch_scan<T, WMAX, 1>(logits, vocab, width, p, pm, ps, pv, pi, err, stream);
 }
 
 template <typename T>
-static hipError_t dispatch_w(const void* logits, int batch, int depth_n, int vocab, int width,
-                             int budget, const ScanPlan& p, const ScanWorkspace& w,
-                             unsigned char* ws, const int32_t* root_token, int32_t* parent,
-                             int32_t* token, int32_t* depth, double* score, int32_t* n_nodes,
-                             int32_t* err, hipStream_t stream) {
-#define JT_BUILD_CASE(WM)                                                                     \
-  case WM:                                                                                   \
-    return launch_build<T, WM>(logits, batch, depth_n, vocab, width, budget, p, w, ws,       \
-                               root_token, parent, token, depth, score, n_nodes, err, stream);
+static void scan_w(const void* logits, int vocab, int width, const ScanPlan& p, float* pm,
+                   double* ps, float* pv, int* pi, int32_t* err, hipStream_t stream) {
   switch (p.wmax) {
-    JT_BUILD_CASE(1)
-    JT_BUILD_CASE(2)
-    JT_BUILD_CASE(4)
-    JT_BUILD_CASE(8)
-    JT_BUILD_CASE(16)
+    case 1: scan_vec<T, 1>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
+    case 2: scan_vec<T, 2>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
+    case 4: scan_vec<T, 4>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
+    case 8: scan_vec<T, 8>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
+    default: scan_vec<T, 16>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
   }
-#undef JT_BUILD_CASE
-  return hipErrorInvalidValue;
+}
+
+template <int WMAX>
+static void select_n(int batch, int depth_n, int width, int budget, const ScanPlan& p,
+                     const float* pm, const double* ps, const float* pv, const int* pi,
+                     const int32_t* root_token, int32_t* parent, int32_t* token, int32_t* depth,
+                     double* score, int32_t* n_nodes, int32_t* err, hipStream_t stream) {
+  const SelectLayout L = select_layout(depth_n, width, budget, WMAX);
+  if (depth_n <= 16)
+    hipLaunchKernelGGL((tree_select<WMAX, 16>), dim3(batch), dim3(kSelectThreads), L.bytes, stream,
+                       pm, ps, pv, pi, p.chunks, depth_n, width, budget, L, root_token, parent,
+                       token, depth, score, n_nodes, err);
+  else
+    hipLaunchKernelGGL((tree_select<WMAX, 64>), dim3(batch), dim3(kSelectThreads), L.bytes, stream,
+                       pm, ps, pv, pi, p.chunks, depth_n, width, budget, L, root_token, parent,
+                       token, depth, score, n_nodes, err);
 }
 
 hipError_t build_tree_launch(const void* logits, jt_dtype dt, int batch, int depth_n, int vocab,
                              int width, int budget, const int32_t* root_token, int32_t* parent,
                              int32_t* token, int32_t* depth, double* score, int32_t* n_nodes,
                              int32_t* err, void* workspace, hipStream_t stream) {
-  const ScanPlan p = scan_plan(batch, depth_n, vocab, width);
-  const ScanWorkspace w = scan_workspace(p, width);
+  const int vec_elems = dt == JT_F32 ? 4 : 8;
+  const bool vec_ok = vocab % vec_elems == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
+  const ScanPlan p = scan_plan(batch, depth_n, vocab, width, vec_ok ? vec_elems : 1);
+  const ScanPlan p1 = scan_plan(batch, depth_n, vocab, width, 1);
+  const ScanWorkspace w = scan_workspace(p1, width);  // sized for the largest plan
   unsigned char* ws = static_cast<unsigned char*>(workspace);
-  if (dt == JT_F32)
-    return dispatch_w<float>(logits, batch, depth_n, vocab, width, budget, p, w, ws, root_token,
-                             parent, token, depth, score, n_nodes, err, stream);
-  return dispatch_w<uint16_t>(logits, batch, depth_n, vocab, width, budget, p, w, ws, root_token,
-                              parent, token, depth, score, n_nodes, err, stream);
+  float* pm = reinterpret_cast<float*>(ws + w.off_max);
+  double* ps = reinterpret_cast<double*>(ws + w.off_sum);
+  float* pv = reinterpret_cast<float*>(ws + w.off_val);
+  int* pi = reinterpret_cast<int*>(ws + w.off_idx);
+  if (dt == JT_F32) scan_w<float>(logits, vocab, width, p, pm, ps, pv, pi, err, stream);
+  else scan_w<uint16_t>(logits, vocab, width, p, pm, ps, pv, pi, err, stream);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  switch (p.wmax) {
+    case 1: select_n<1>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
+    case 2: select_n<2>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
+    case 4: select_n<4>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
+    case 8: select_n<8>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
+    default: select_n<16>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace jt

@@ -14,6 +14,7 @@ namespace jt {
 // build_tree.hip
 size_t build_tree_workspace_bytes(int batch, int depth_n, int vocab, int width);
 size_t build_tree_lds_bytes(int depth_n, int width, int budget);
+int build_tree_max_vocab();
 hipError_t build_tree_launch(const void* logits, jt_dtype dt, int batch, int depth_n, int vocab,
                              int width, int budget, const int32_t* root_token, int32_t* parent,
                              int32_t* token, int32_t* depth, double* score, int32_t* n_nodes,
