@@ -12,7 +12,7 @@ namespace {
 constexpr int kMaxNodes = 1024;
 constexpr int kMaxDepth = 64;
 constexpr int kMaxWidth = 16;
-constexpr size_t kMaxSelectLds = 64 * 1024;
+constexpr size_t kMaxSelectLds = 160 * 1024;  // gfx950 LDS per workgroup
 
 inline jt_status launched(hipError_t e) { return e == hipSuccess ? JT_OK : JT_ERR_LAUNCH; }
 

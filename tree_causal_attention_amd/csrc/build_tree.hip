@@ -236,9 +236,11 @@ __host__ __device__ inline int level_cap(int d, int width, int budget) {
 struct SelectLayout {
   int tot;         // sum of level capacities
   int capmax;      // max level capacity
-  int top;         // power of two >= capmax (binary-lifting start)
+  int wp;          // power of two >= W (lists merged per level)
+  int np;          // power of two >= N (lists merged across levels)
+  int mstride;     // list stride of the phase-3 merge buffers (>= 1)
   size_t off_S, off_lse, off_cval, off_ctok, off_loff, off_lcnt, off_rawa, off_rawb;
-  size_t off_score, off_info, off_gidx, bytes;
+  size_t off_score, off_info, off_gidx, off_ms0, off_ms1, off_mi0, off_mi1, off_len, bytes;
 };
 
 inline SelectLayout select_layout(int depth_n, int width, int budget, int wmax) {
@@ -250,8 +252,13 @@ inline SelectLayout select_layout(int depth_n, int width, int budget, int wmax) 
     L.tot += c;
     L.capmax = std::max(L.capmax, c);
   }
-  L.top = 1;
-  while (L.top < L.capmax) L.top <<= 1;
+  L.wp = 1;
+  while (L.wp < width) L.wp <<= 1;
+  L.np = 1;
+  while (L.np < depth_n) L.np <<= 1;
+  L.mstride = std::max(1, budget);
+  const size_t mcount = std::max(static_cast<size_t>(L.wp) * L.capmax,
+                                 static_cast<size_t>(L.np) * L.mstride);
   size_t o = 0;
   auto take = [&](size_t n, size_t align) { o = (o + align - 1) / align * align; size_t r = o; o += n; return r; };
   L.off_S = take(sizeof(double) * (depth_n + 1), 8);
@@ -259,11 +266,16 @@ inline SelectLayout select_layout(int depth_n, int width, int budget, int wmax) 
   L.off_rawa = take(sizeof(double) * L.capmax, 8);
   L.off_rawb = take(sizeof(double) * L.capmax, 8);
   L.off_score = take(sizeof(double) * std::max(1, L.tot), 8);
+  L.off_ms0 = take(sizeof(double) * L.wp * L.capmax, 8);
+  L.off_ms1 = take(sizeof(double) * L.wp * L.capmax, 8);
   L.off_cval = take(sizeof(float) * depth_n * wmax, 4);
   L.off_ctok = take(sizeof(int) * depth_n * wmax, 4);
   L.off_loff = take(sizeof(int) * (depth_n + 2), 4);
   L.off_lcnt = take(sizeof(int) * (depth_n + 2), 4);
   L.off_info = take(sizeof(uint32_t) * std::max(1, L.tot), 4);
+  L.off_mi0 = take(sizeof(uint32_t) * mcount, 4);
+  L.off_mi1 = take(sizeof(uint32_t) * mcount, 4);
+  L.off_len = take(sizeof(int) * 2 * std::max(L.wp, L.np), 4);
   L.off_gidx = take(sizeof(uint16_t) * std::max(1, L.tot), 2);
   L.bytes = (o + 15) / 16 * 16;
   return L;
@@ -287,10 +299,36 @@ __device__ __noinline__ bool precedes_tied(const double* score, const uint32_t* 
   }
 }
 
-// Binary lifting over a prefix-true predicate runs a fixed number of steps
-// (top = a power of two >= every list length), so the W - 1 (or N - 1)
-// searches of one candidate advance in lockstep and their LDS reads overlap.
-template <int WMAX, int NMAX>
+// Same-level order of two candidates (score, info = parent position | rank << 16).
+__device__ __forceinline__ bool precedes_level(double sa, uint32_t ia, double sb, uint32_t ib) {
+  if (sa != sb) return sa > sb;
+  const uint32_t pa = ia & 0xFFFFu, pb = ib & 0xFFFFu;
+  if (pa != pb) return pa < pb;
+  return (ia >> 16) < (ib >> 16);
+}
+
+// Merge path: number of elements of A among the first o outputs of merge(A, B)
+// under a strict order (A[i-1] precedes B[o-i] holds exactly for i <= answer).
+template <typename Prec>
+__device__ __forceinline__ int co_rank(int o, int la, int lb, Prec prec_ab) {
+  int lo = max(0, o - lb), hi = min(o, la);
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (prec_ab(mid - 1, o - mid)) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// One workgroup per sequence.
+//  phase 1: per depth, merge the chunk partials (lse, top-W).
+//  phase 2: per level d, the W candidate columns (children of the sorted level
+//    d-1 by rank k; each column sorted, pruned to the first cap_d/(k+1) rows)
+//    are merged pairwise (merge path, log2 W rounds) into the sorted level,
+//    truncated to cap_d.
+//  phase 3: the sorted levels are merged pairwise (log2 N rounds, truncated to
+//    B) under the global key; the merged position is the node index.
+//  phase 4: write parent/token/depth/score in node order.
+template <int WMAX>
 __global__ __launch_bounds__(kSelectThreads) void tree_select(
     const float* __restrict__ part_max, const double* __restrict__ part_sum,
     const float* __restrict__ part_val, const int* __restrict__ part_idx, int chunks, int depth_n,
@@ -303,17 +341,22 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   double* raw_a = reinterpret_cast<double*>(smem + L.off_rawa);
   double* raw_b = reinterpret_cast<double*>(smem + L.off_rawb);
   double* lv_score = reinterpret_cast<double*>(smem + L.off_score);
+  double* ms[2] = {reinterpret_cast<double*>(smem + L.off_ms0),
+                   reinterpret_cast<double*>(smem + L.off_ms1)};
   float* cval = reinterpret_cast<float*>(smem + L.off_cval);
   int* ctok = reinterpret_cast<int*>(smem + L.off_ctok);
   int* loff = reinterpret_cast<int*>(smem + L.off_loff);
   int* lcnt = reinterpret_cast<int*>(smem + L.off_lcnt);
   uint32_t* lv_info = reinterpret_cast<uint32_t*>(smem + L.off_info);
+  uint32_t* mi[2] = {reinterpret_cast<uint32_t*>(smem + L.off_mi0),
+                     reinterpret_cast<uint32_t*>(smem + L.off_mi1)};
+  int* lens = reinterpret_cast<int*>(smem + L.off_len);  // [2][max(wp, np)]
   uint16_t* lv_gidx = reinterpret_cast<uint16_t*>(smem + L.off_gidx);
+  const int lstride = max(L.wp, L.np);
 
   const int seq = blockIdx.x;
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int nwaves = kSelectThreads / kWave;
-  const int top = L.top;
 
   // ---- phase 1: merge the chunk partials of every depth (one wave a depth);
   // each lane holds one chunk's sorted candidates in registers.
@@ -370,9 +413,10 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
     loff[depth_n + 1] = o;
     raw_a[0] = 0.0;
   }
+  for (int x = tid; x < L.tot; x += kSelectThreads) lv_gidx[x] = 0xFFFF;
   __syncthreads();
 
-  // ---- phase 2: level by level, keep the best cap_d children, in order
+  // ---- phase 2: level by level, the best cap_d children in key order
   double* raw_prev = raw_a;
   double* raw_cur = raw_b;
   int m_prev = 1;
@@ -381,43 +425,49 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
     const int cap = level_cap(d, width, budget);
     if (cap <= 0 || m_prev == 0) break;
     const double Sd = S[d];
-    double cv[WMAX];
-#pragma unroll
-    for (int k = 0; k < WMAX; ++k) cv[k] = static_cast<double>(cval[(d - 1) * WMAX + (k < width ? k : 0)]);
-    const int ncand = m_prev * width;
-    for (int idx = tid; idx < ncand; idx += kSelectThreads) {
-      const int k = idx / m_prev, p = idx % m_prev;
-      if ((p + 1) * (k + 1) > cap) continue;
-      double vk = cv[0];
-#pragma unroll
-      for (int kk = 1; kk < WMAX; ++kk) vk = (kk == k) ? cv[kk] : vk;
-      const double raw = raw_prev[p] + vk;
-      const double sc = raw - Sd;
-      int cnt[WMAX];
-#pragma unroll
-      for (int k2 = 0; k2 < WMAX; ++k2) cnt[k2] = 0;
-      for (int sz = top; sz > 0; sz >>= 1) {
-        // branch-free step: every column's read is issued before any compare
-#pragma unroll
-        for (int k2 = 0; k2 < WMAX; ++k2) {
-          const int mid = cnt[k2] + sz;
-          const int q = min(mid, m_prev) - 1;
-          const double s2 = (raw_prev[q] + cv[k2]) - Sd;
-          const bool pred = k2 < width && k2 != k && mid <= m_prev &&
-                            (s2 > sc || (s2 == sc && (k2 < k ? q <= p : q < p)));
-          cnt[k2] = pred ? mid : cnt[k2];
-        }
-      }
-      int r = p;
-#pragma unroll
-      for (int k2 = 0; k2 < WMAX; ++k2) r += cnt[k2];
-      if (r < cap) {
-        lv_score[loff[d] + r] = sc;
-        lv_info[loff[d] + r] = static_cast<uint32_t>(p) | (static_cast<uint32_t>(k) << 16);
-        raw_cur[r] = raw;
+    // columns: list k holds children (p, k), p < len_k, at ms/mi[0] + k * cap
+    for (int idx = tid; idx < L.wp * cap; idx += kSelectThreads) {
+      const int k = idx / cap, p = idx % cap;
+      const int len_k = k < width ? min(m_prev, cap / (k + 1)) : 0;
+      if (p < len_k) {
+        ms[0][idx] = (raw_prev[p] + static_cast<double>(cval[(d - 1) * WMAX + k])) - Sd;
+        mi[0][idx] = static_cast<uint32_t>(p) | (static_cast<uint32_t>(k) << 16);
       }
     }
-    const int m_d = min(cap, ncand);
+    if (tid < L.wp) lens[tid] = tid < width ? min(m_prev, cap / (tid + 1)) : 0;
+    __syncthreads();
+    int src = 0;
+    for (int lists = L.wp; lists > 1; lists >>= 1) {
+      const int pairs = lists >> 1;
+      const int* lsrc = lens + src * lstride;
+      int* ldst = lens + (src ^ 1) * lstride;
+      for (int idx = tid; idx < pairs * cap; idx += kSelectThreads) {
+        const int q = idx / cap, o = idx % cap;
+        const int la = lsrc[2 * q], lb = lsrc[2 * q + 1];
+        if (o >= min(cap, la + lb)) continue;
+        const double* As = ms[src] + (2 * q) * cap;
+        const uint32_t* Ai = mi[src] + (2 * q) * cap;
+        const double* Bs = As + cap;
+        const uint32_t* Bi = Ai + cap;
+        const int i = co_rank(o, la, lb, [&](int ia, int jb) {
+          return precedes_level(As[ia], Ai[ia], Bs[jb], Bi[jb]);
+        });
+        const int j = o - i;
+        const bool take_a = i < la && (j >= lb || precedes_level(As[i], Ai[i], Bs[j], Bi[j]));
+        ms[src ^ 1][q * cap + o] = take_a ? As[i] : Bs[j];
+        mi[src ^ 1][q * cap + o] = take_a ? Ai[i] : Bi[j];
+      }
+      if (tid < pairs) ldst[tid] = min(cap, lsrc[2 * tid] + lsrc[2 * tid + 1]);
+      __syncthreads();
+      src ^= 1;
+    }
+    const int m_d = lens[src * lstride];
+    for (int o = tid; o < m_d; o += kSelectThreads) {
+      const uint32_t inf = mi[src][o];
+      lv_score[loff[d] + o] = ms[src][o];
+      lv_info[loff[d] + o] = inf;
+      raw_cur[o] = raw_prev[inf & 0xFFFFu] + static_cast<double>(cval[(d - 1) * WMAX + (inf >> 16)]);
+    }
     if (tid == 0) lcnt[d] = m_d;
     __syncthreads();
     double* t = raw_prev; raw_prev = raw_cur; raw_cur = t;
@@ -428,62 +478,56 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
     for (int d = last_level + 1; d <= depth_n; ++d) lcnt[d] = 0;
   __syncthreads();
 
-  // ---- phase 3: global rank of every kept node (lockstep searches over levels)
-  int lo_r[NMAX], lc_r[NMAX];
-  int total = 0;
-#pragma unroll
-  for (int d2 = 0; d2 < NMAX; ++d2) {
-    lo_r[d2] = (d2 + 1 <= depth_n) ? loff[d2 + 1] : 0;
-    lc_r[d2] = (d2 + 1 <= depth_n) ? lcnt[d2 + 1] : 0;
-    total += lc_r[d2];
+  // ---- phase 3: merge the sorted levels into the global order
+  const int B = L.mstride;
+  for (int idx = tid; idx < L.np * B; idx += kSelectThreads) {
+    const int l = idx / B, o = idx % B;
+    if (l < depth_n && o < lcnt[l + 1])
+      mi[0][idx] = (static_cast<uint32_t>(l + 1) << 16) | static_cast<uint32_t>(o);
   }
-  const int n_sel = min(budget, total);
-  for (int idx = tid; idx < loff[depth_n + 1]; idx += kSelectThreads) {
-    int d = 1;
-    while (idx >= loff[d + 1]) ++d;
-    const int i = idx - loff[d];
-    if (i >= lcnt[d]) continue;
-    const double sx = lv_score[idx];
-    int cnt[NMAX];
-#pragma unroll
-    for (int d2 = 0; d2 < NMAX; ++d2) cnt[d2] = 0;
-    for (int sz = top; sz > 0; sz >>= 1) {
-      // fast path branch-free; exact cross-level score ties (rare) resolved after
-      bool tie[NMAX];
-      bool any_tie = false;
-#pragma unroll
-      for (int d2 = 0; d2 < NMAX; ++d2) {
-        const int mid = cnt[d2] + sz;
-        const bool ok = d2 + 1 != d && mid <= lc_r[d2];
-        const int q = max(0, min(mid, lc_r[d2]) - 1);
-        const double sy = lv_score[lo_r[d2] + q];
-        tie[d2] = ok && sy == sx;
-        any_tie |= tie[d2];
-        cnt[d2] = (ok && sy > sx) ? mid : cnt[d2];
-      }
-      if (any_tie) {
-#pragma unroll
-        for (int d2 = 0; d2 < NMAX; ++d2)
-          if (tie[d2] && precedes_tied(lv_score, lv_info, loff, d2 + 1, cnt[d2] + sz - 1, d, i))
-            cnt[d2] += sz;
-      }
+  if (tid < L.np) lens[tid] = tid < depth_n ? min(B, lcnt[tid + 1]) : 0;
+  __syncthreads();
+  auto prec_cross = [&](uint32_t ra, uint32_t rb) {
+    const int da = static_cast<int>(ra >> 16), ia = static_cast<int>(ra & 0xFFFFu);
+    const int db = static_cast<int>(rb >> 16), ib = static_cast<int>(rb & 0xFFFFu);
+    const double sa = lv_score[loff[da] + ia], sb = lv_score[loff[db] + ib];
+    if (sa != sb) return sa > sb;
+    return precedes_tied(lv_score, lv_info, loff, da, ia, db, ib);
+  };
+  int src = 0;
+  for (int lists = L.np; lists > 1; lists >>= 1) {
+    const int pairs = lists >> 1;
+    const int* lsrc = lens + src * lstride;
+    int* ldst = lens + (src ^ 1) * lstride;
+    for (int idx = tid; idx < pairs * B; idx += kSelectThreads) {
+      const int q = idx / B, o = idx % B;
+      const int la = lsrc[2 * q], lb = lsrc[2 * q + 1];
+      if (o >= min(B, la + lb)) continue;
+      const uint32_t* A = mi[src] + (2 * q) * B;
+      const uint32_t* Bv = A + B;
+      const int i = co_rank(o, la, lb, [&](int ia, int jb) { return prec_cross(A[ia], Bv[jb]); });
+      const int j = o - i;
+      const bool take_a = i < la && (j >= lb || prec_cross(A[i], Bv[j]));
+      mi[src ^ 1][q * B + o] = take_a ? A[i] : Bv[j];
     }
-    int R = i;
-#pragma unroll
-    for (int d2 = 0; d2 < NMAX; ++d2) R += cnt[d2];
-    lv_gidx[idx] = (R < budget) ? static_cast<uint16_t>(R + 1) : static_cast<uint16_t>(0xFFFF);
+    if (tid < pairs) ldst[tid] = min(B, lsrc[2 * tid] + lsrc[2 * tid + 1]);
+    __syncthreads();
+    src ^= 1;
+  }
+  const int n_sel = min(budget, lens[src * lstride]);
+  for (int o = tid; o < n_sel; o += kSelectThreads) {
+    const uint32_t r = mi[src][o];
+    lv_gidx[loff[r >> 16] + (r & 0xFFFFu)] = static_cast<uint16_t>(o + 1);
   }
   __syncthreads();
 
   // ---- phase 4: write the tree in node-index order
   const size_t base = static_cast<size_t>(seq) * (budget + 1);
-  for (int idx = tid; idx < loff[depth_n + 1]; idx += kSelectThreads) {
-    int d = 1;
-    while (idx >= loff[d + 1]) ++d;
-    const int i = idx - loff[d];
-    if (i >= lcnt[d]) continue;
-    const int g = lv_gidx[idx];
-    if (g == 0xFFFF) continue;
+  for (int o = tid; o < n_sel; o += kSelectThreads) {
+    const uint32_t r = mi[src][o];
+    const int d = static_cast<int>(r >> 16), i = static_cast<int>(r & 0xFFFFu);
+    const int idx = loff[d] + i;
+    const int g = o + 1;
     const uint32_t inf = lv_info[idx];
     const int pp = static_cast<int>(inf & 0xFFFFu), k = static_cast<int>(inf >> 16);
     parent[base + g] = (d == 1) ? 0 : static_cast<int32_t>(lv_gidx[loff[d - 1] + pp]);
@@ -597,14 +641,13 @@ static void select_n(int batch, int depth_n, int width, int budget, const ScanPl
                      const int32_t* root_token, int32_t* parent, int32_t* token, int32_t* depth,
                      double* score, int32_t* n_nodes, int32_t* err, hipStream_t stream) {
   const SelectLayout L = select_layout(depth_n, width, budget, WMAX);
-  if (depth_n <= 16)
-    hipLaunchKernelGGL((tree_select<WMAX, 16>), dim3(batch), dim3(kSelectThreads), L.bytes, stream,
-                       pm, ps, pv, pi, p.chunks, depth_n, width, budget, L, root_token, parent,
-                       token, depth, score, n_nodes, err);
-  else
-    hipLaunchKernelGGL((tree_select<WMAX, 64>), dim3(batch), dim3(kSelectThreads), L.bytes, stream,
-                       pm, ps, pv, pi, p.chunks, depth_n, width, budget, L, root_token, parent,
-                       token, depth, score, n_nodes, err);
+  if (L.bytes > 64 * 1024)
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tree_select<WMAX>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize,
+                              static_cast<int>(L.bytes));
+  hipLaunchKernelGGL((tree_select<WMAX>), dim3(batch), dim3(kSelectThreads), L.bytes, stream, pm,
+                     ps, pv, pi, p.chunks, depth_n, width, budget, L, root_token, parent, token,
+                     depth, score, n_nodes, err);
 }
 
 hipError_t build_tree_launch(const void* logits, jt_dtype dt, int batch, int depth_n, int vocab,

@@ -11,8 +11,8 @@
 //   * The page ids of the item's key range are staged in LDS first, so tile
 //     loads never wait on a page-table lookup.
 //   * K and V of 4 pages (64 keys) are gathered with 16-byte loads one tile
-//     ahead (register staging) and stored row-major [key][dim] in LDS with a
-//     16-byte-chunk XOR swizzle (chunk ^ key % 8) against bank conflicts.
+//     ahead (register staging) and stored row-major [key][dim] in LDS, rows
+//     padded (+16 B for K, +32 B for V) against bank conflicts.
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys as M, queries as N, so
 //     each lane owns one query column and the softmax reductions stay in-lane
 //     plus one cross-half exchange); Q stays in registers.
@@ -100,6 +100,10 @@ struct Item {
   int s, g, sg, rt, sp, splits;
 };
 
+// 16 zero chunks of 16 bytes (global memory, never written): the source of
+// K/V loads for keys that do not exist, so the loads never need a branch.
+__device__ uint4 g_zero16[16];
+
 // Maps the linear workgroup id to a work item; false for padding slots.
 __device__ __forceinline__ bool decode_item(const AttnArgs& a, int L, Item& it) {
   const int xcd = L % kXcds, slot = L / kXcds;
@@ -138,8 +142,14 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   constexpr int DB = D / 32;                 // 32-row blocks of O^T
   constexpr int KS = D / 16;                 // MFMA k-steps of K Q^T
 
-  __shared__ __align__(16) uint16_t k_lds[2][kKT * D];
-  __shared__ __align__(16) uint16_t v_lds[2][kKT * D];
+  // Row strides padded by 16 B (K) and 32 B (V): the K fragment reads (32 keys
+  // at one 16-byte column) and the transposing V reads (4 keys x 32 bytes per
+  // 16 lanes) then spread over all banks, and every LDS address is a per-lane
+  // base plus a compile-time offset.
+  constexpr int KSTR = D + 8;
+  constexpr int VSTR = D + 16;
+  __shared__ __align__(16) uint16_t k_lds[2][kKT * KSTR];
+  __shared__ __align__(16) uint16_t v_lds[2][kKT * VSTR];
   __shared__ int pg_lds[kMaxPagesLds];
 
   Item item;
@@ -193,6 +203,9 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
       qreg[kk] = __builtin_bit_cast(bf16x8, u);
     }
   }
+  // Drain the Q loads here: otherwise the wait for them lands inside the tile
+  // loop and also waits for each freshly issued K/V prefetch.
+  __builtin_amdgcn_s_waitcnt(0);
   const uint32_t* anc_row = a.anc + (static_cast<size_t>(s) * a.max_nodes + node) * a.nwords;
   const size_t head_stride = static_cast<size_t>(kPage) * D;
   const size_t page_stride = static_cast<size_t>(a.hkv) * head_stride;
@@ -210,35 +223,45 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   float m_run = -INFINITY;  // running max in scaled (log2) units
   float l_run = 0.0f;       // this lane's half of the normaliser
 
-  // ---- global -> registers -> LDS (two tiles in flight)
-  uint4 kreg[LPT], vreg[LPT];
-  auto fetch = [&](int t0, uint4 (&kr)[LPT], uint4 (&vr)[LPT]) {
-#pragma unroll
-    for (int c = 0; c < LPT; ++c) {
-      const int e = tid + c * kAttnThreads;
-      const int key = e / CPK, ch = e % CPK;
-      const int t = t0 + key;
-      uint4 ku = make_uint4(0, 0, 0, 0), vu = make_uint4(0, 0, 0, 0);
-      if (t < kv_len) {
-        const int p = pg_lds[t / kPage - pg0];
-        if (p >= 0) {
-          const size_t off = p * page_stride + (t % kPage) * D + ch * 8;
-          ku = *reinterpret_cast<const uint4*>(kbase + off);
-          vu = *reinterpret_cast<const uint4*>(vbase + off);
-        }
-      }
-      kr[c] = ku;
-      vr[c] = vu;
+  // ---- global -> registers -> LDS, one tile ahead.  Branch-free: keys past
+  // the sequence (and pages flagged bad) read a block of zeros.
+  static_assert(LPT == 1 || LPT == 2, "staging is written for 1 or 2 chunks per thread");
+  uint4 kr0, vr0, kr1, vr1;
+  auto src_off = [&](int t0, int c, const uint16_t*& kp, const uint16_t*& vp) {
+    const int e = tid + c * kAttnThreads;
+    const int key = e / CPK, ch = e % CPK;
+    const int t = t0 + key;
+    const int p = (t < kv_len) ? pg_lds[t / kPage - pg0] : -1;
+    kp = reinterpret_cast<const uint16_t*>(g_zero16) + ch * 8;
+    vp = kp;
+    if (p >= 0) {
+      const size_t off = p * page_stride + (t % kPage) * D + ch * 8;
+      kp = kbase + off;
+      vp = vbase + off;
     }
   };
-  auto stash = [&](int buf, const uint4 (&kr)[LPT], const uint4 (&vr)[LPT]) {
-#pragma unroll
-    for (int c = 0; c < LPT; ++c) {
-      const int e = tid + c * kAttnThreads;
+  auto fetch = [&](int t0) {
+    const uint16_t *kp, *vp;
+    src_off(t0, 0, kp, vp);
+    kr0 = *reinterpret_cast<const uint4*>(kp);
+    vr0 = *reinterpret_cast<const uint4*>(vp);
+    if constexpr (LPT == 2) {
+      src_off(t0, 1, kp, vp);
+      kr1 = *reinterpret_cast<const uint4*>(kp);
+      vr1 = *reinterpret_cast<const uint4*>(vp);
+    }
+  };
+  auto stash = [&](int buf) {
+    {
+      const int key = tid / CPK, ch = tid % CPK;
+      *reinterpret_cast<uint4*>(&k_lds[buf][key * KSTR + ch * 8]) = kr0;
+      *reinterpret_cast<uint4*>(&v_lds[buf][key * VSTR + ch * 8]) = vr0;
+    }
+    if constexpr (LPT == 2) {
+      const int e = tid + kAttnThreads;
       const int key = e / CPK, ch = e % CPK;
-      const int o = key * D + ((ch ^ (key & 7)) * 8);
-      *reinterpret_cast<uint4*>(&k_lds[buf][o]) = kr[c];
-      *reinterpret_cast<uint4*>(&v_lds[buf][o]) = vr[c];
+      *reinterpret_cast<uint4*>(&k_lds[buf][key * KSTR + ch * 8]) = kr1;
+      *reinterpret_cast<uint4*>(&v_lds[buf][key * VSTR + ch * 8]) = vr1;
     }
   };
 
@@ -254,9 +277,8 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const int key = kb * 32 + col;
-        const int c = 2 * kk + h;
         const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&k_lds[buf][key * D + ((c ^ (key & 7)) * 8)]);
+            *reinterpret_cast<const bf16x8*>(&k_lds[buf][key * KSTR + 16 * kk + 8 * h]);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kk], sacc[kb], 0, 0, 0);
       }
     }
@@ -324,13 +346,12 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
         const int dst = 32 * db + 16 * (tg & 1) + 4 * tq;
-        const int ch = dst >> 3, off = dst & 7;
         const int ka = 16 * ks + 4 * h + tk;
         const int kc = ka + 8;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_ptr)(&v_lds[buf][ka * D + ((ch ^ (ka & 7)) * 8) + off]));
+            (lds_i16x4_ptr)(&v_lds[buf][ka * VSTR + dst]));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_ptr)(&v_lds[buf][kc * D + ((ch ^ (kc & 7)) * 8) + off]));
+            (lds_i16x4_ptr)(&v_lds[buf][kc * VSTR + dst]));
         const uint2 ulo = __builtin_bit_cast(uint2, lo);
         const uint2 uhi = __builtin_bit_cast(uint2, hi);
         const uint4 u = make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
@@ -344,15 +365,15 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   // Iteration it computes tile it from LDS buffer (it - tb) & 1 while tile it+1
   // is loading into registers; it is stored to the other buffer afterwards.
   if (tb < te) {
-    fetch(tb * kKT, kreg, vreg);
-    stash(0, kreg, vreg);
+    fetch(tb * kKT);
+    stash(0);
   }
   __syncthreads();
   for (int it = tb; it < te; ++it) {
     const int buf = (it - tb) & 1;
-    if (it + 1 < te) fetch((it + 1) * kKT, kreg, vreg);
+    if (it + 1 < te) fetch((it + 1) * kKT);
     compute(buf, it * kKT);
-    if (it + 1 < te) stash(buf ^ 1, kreg, vreg);
+    if (it + 1 < te) stash(buf ^ 1);
     __syncthreads();
   }
 
