@@ -54,6 +54,9 @@ constexpr int kXcds = 8;             // MI355X: 8 XCDs, workgroups dealt round-r
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 // Work decomposition (identical for every (sequence, KV head) group; a
 // group's actual row count and key range are read on the device):
@@ -100,9 +103,10 @@ struct Item {
   int s, g, sg, rt, sp, splits;
 };
 
-// 16 zero chunks of 16 bytes (global memory, never written): the source of
-// K/V loads for keys that do not exist, so the loads never need a branch.
-__device__ uint4 g_zero16[16];
+// One page of zeros for the widest head (global memory, never written): K/V
+// loads of pages that do not exist (past the sequence, or flagged bad) read
+// it, so the loads never branch.
+__device__ uint4 g_zero_page[kPage * 128 * 2 / 16];
 
 // Maps the linear workgroup id to a work item; false for padding slots.
 __device__ __forceinline__ bool decode_item(const AttnArgs& a, int L, Item& it) {
@@ -150,7 +154,7 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   constexpr int VSTR = D + 16;
   __shared__ __align__(16) uint16_t k_lds[2][kKT * KSTR];
   __shared__ __align__(16) uint16_t v_lds[2][kKT * VSTR];
-  __shared__ int pg_lds[kMaxPagesLds];
+  __shared__ __align__(16) int pg_lds[kMaxPagesLds];
 
   Item item;
   if (!decode_item(a, blockIdx.x, item)) return;
@@ -172,17 +176,21 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   const int tb = static_cast<int>(static_cast<long long>(ntiles) * item.sp / item.splits);
   const int te = static_cast<int>(static_cast<long long>(ntiles) * (item.sp + 1) / item.splits);
 
-  // ---- page ids of this item's key range, staged in LDS
+  // ---- page ids of this item's key range, staged in LDS (-1: no page)
   const int kv_len = P + n;
   const int pg0 = tb * (kKT / kPage);
-  const int npg = max(0, min(te * (kKT / kPage), (kv_len + kPage - 1) / kPage) - pg0);
+  const int nslots = (te - tb) * (kKT / kPage);
+  const int pg_end = (kv_len + kPage - 1) / kPage;
   {
     const int32_t* ptab = a.page_table + static_cast<size_t>(s) * a.max_pages;
-    for (int i = tid; i < npg; i += kAttnThreads) {
-      int p = ptab[pg0 + i];
-      if (p < 0 || p >= a.num_pages) {
-        report(a.err, JT_DERR_BAD_PAGE);
-        p = -1;
+    for (int i = tid; i < nslots; i += kAttnThreads) {
+      int p = -1;
+      if (pg0 + i < pg_end) {
+        p = ptab[pg0 + i];
+        if (p < 0 || p >= a.num_pages) {
+          report(a.err, JT_DERR_BAD_PAGE);
+          p = -1;
+        }
       }
       pg_lds[i] = p;
     }
@@ -223,51 +231,67 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   float m_run = -INFINITY;  // running max in scaled (log2) units
   float l_run = 0.0f;       // this lane's half of the normaliser
 
-  // ---- global -> registers -> LDS, one tile ahead.  Branch-free: keys past
-  // the sequence (and pages flagged bad) read a block of zeros.
+  // ---- global -> registers -> LDS.  Thread tid moves the 16-byte chunks
+  // (key tid / CPK + c * 512 / CPK, column tid % CPK) of a tile; the keys of
+  // one wave's chunk lie in one page, so the page base is wave-uniform (scalar
+  // registers) and each lane adds a fixed offset inside the page.
   static_assert(LPT == 1 || LPT == 2, "staging is written for 1 or 2 chunks per thread");
-  uint4 kr0, vr0, kr1, vr1;
-  auto src_off = [&](int t0, int c, const uint16_t*& kp, const uint16_t*& vp) {
-    const int e = tid + c * kAttnThreads;
-    const int key = e / CPK, ch = e % CPK;
-    const int t = t0 + key;
-    const int p = (t < kv_len) ? pg_lds[t / kPage - pg0] : -1;
-    kp = reinterpret_cast<const uint16_t*>(g_zero16) + ch * 8;
-    vp = kp;
-    if (p >= 0) {
-      const size_t off = p * page_stride + (t % kPage) * D + ch * 8;
-      kp = kbase + off;
-      vp = vbase + off;
-    }
+  static_assert(kPage % (kWave / CPK) == 0, "a wave's chunk must not straddle pages");
+  const int inner = ((tid / CPK) % kPage) * D + (tid % CPK) * 8;
+  // Page ids a wave needs for one tile (slot of chunk c inside the tile's 4
+  // pages), read from LDS one tile before the loads they address, so turning
+  // them into scalar bases never waits on LDS.
+  auto page_ids = [&](int tile, int (&pid)[LPT]) __attribute__((always_inline)) {
+    const int t = min(tile, te - 1) - tb;  // clamped: the last tile's ids stay in range
+#pragma unroll
+    for (int c = 0; c < LPT; ++c)
+      pid[c] = pg_lds[t * (kKT / kPage) + (w * (kWave / CPK) + c * (kAttnThreads / CPK)) / kPage];
   };
-  auto fetch = [&](int t0) {
-    const uint16_t *kp, *vp;
-    src_off(t0, 0, kp, vp);
-    kr0 = *reinterpret_cast<const uint4*>(kp);
-    vr0 = *reinterpret_cast<const uint4*>(vp);
-    if constexpr (LPT == 2) {
-      src_off(t0, 1, kp, vp);
-      kr1 = *reinterpret_cast<const uint4*>(kp);
-      vr1 = *reinterpret_cast<const uint4*>(vp);
-    }
+  auto chunk_ptr = [&](const uint16_t* base, int pid) __attribute__((always_inline)) {
+    const int p = __builtin_amdgcn_readfirstlane(pid);
+    const uint16_t* pb = (p >= 0) ? base + static_cast<size_t>(p) * page_stride
+                                  : reinterpret_cast<const uint16_t*>(g_zero_page);
+    return reinterpret_cast<const uint4*>(pb + inner);
   };
-  auto stash = [&](int buf) {
-    {
-      const int key = tid / CPK, ch = tid % CPK;
-      *reinterpret_cast<uint4*>(&k_lds[buf][key * KSTR + ch * 8]) = kr0;
-      *reinterpret_cast<uint4*>(&v_lds[buf][key * VSTR + ch * 8]) = vr0;
-    }
+  uint4 kr0, kr1, vr0, vr1;
+  int pk[LPT], pv_[LPT];  // page ids of the next K and V loads
+  auto fetch_k = [&]() __attribute__((always_inline)) {
+    kr0 = *chunk_ptr(kbase, pk[0]);
+    if constexpr (LPT == 2) kr1 = *chunk_ptr(kbase, pk[1]);
+  };
+  auto fetch_v = [&]() __attribute__((always_inline)) {
+    vr0 = *chunk_ptr(vbase, pv_[0]);
+    if constexpr (LPT == 2) vr1 = *chunk_ptr(vbase, pv_[1]);
+  };
+  auto stash_k = [&](int buf) __attribute__((always_inline)) {
+    *reinterpret_cast<uint4*>(&k_lds[buf][(tid / CPK) * KSTR + (tid % CPK) * 8]) = kr0;
     if constexpr (LPT == 2) {
       const int e = tid + kAttnThreads;
-      const int key = e / CPK, ch = e % CPK;
-      *reinterpret_cast<uint4*>(&k_lds[buf][key * KSTR + ch * 8]) = kr1;
-      *reinterpret_cast<uint4*>(&v_lds[buf][key * VSTR + ch * 8]) = vr1;
+      *reinterpret_cast<uint4*>(&k_lds[buf][(e / CPK) * KSTR + (e % CPK) * 8]) = kr1;
+    }
+  };
+  // Keys past the sequence inside its last page hold whatever the pool holds
+  // there: their scores are masked, and their V rows are zeroed here so a
+  // zero weight never meets a non-finite value.
+  auto stash_v = [&](int buf, int t0) __attribute__((always_inline)) {
+    if (t0 + kKT > kv_len) {
+      const uint4 z = make_uint4(0, 0, 0, 0);
+      if (t0 + tid / CPK >= kv_len) vr0 = z;
+      if constexpr (LPT == 2)
+        if (t0 + (tid + kAttnThreads) / CPK >= kv_len) vr1 = z;
+    }
+    *reinterpret_cast<uint4*>(&v_lds[buf][(tid / CPK) * VSTR + (tid % CPK) * 8]) = vr0;
+    if constexpr (LPT == 2) {
+      const int e = tid + kAttnThreads;
+      *reinterpret_cast<uint4*>(&v_lds[buf][(e / CPK) * VSTR + (e % CPK) * 8]) = vr1;
     }
   };
 
-  auto compute = [&](int buf, int t0) {
-    // ---- S^T = K Q^T for 2 blocks of 32 keys (independent accumulators interleaved)
-    f32x16 sacc[2];
+  f32x16 sacc[2];  // S^T of the tile between its QK and softmax phases
+  bf16x8 pf[4];    // P^T of the tile between its softmax and PV phases
+
+  // S^T = K Q^T for 2 blocks of 32 keys (independent accumulators interleaved)
+  auto qk = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -282,8 +306,11 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kk], sacc[kb], 0, 0, 0);
       }
     }
+  };
 
-    // ---- mask (only tiles that reach the tree tail)
+  // mask (only tiles that reach the tree tail), then online softmax in base 2
+  // with a lazy rescale
+  auto softmax = [&](int t0) __attribute__((always_inline)) {
     if (t0 + kKT > P) {
       const int jb = t0 - P;  // tail index of the tile's first key (may be < 0)
       const int w0 = (jb >= 0) ? (jb >> 5) : -((-jb + 31) >> 5);
@@ -295,18 +322,18 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
         wd[k] = (row_ok && wi >= 0 && wi < a.nwords) ? anc_row[wi] : 0u;
       }
       const uint64_t lo = (static_cast<uint64_t>(wd[1]) << 32) | wd[0];
-      const uint64_t win = (lo >> sh) | (sh ? (static_cast<uint64_t>(wd[2]) << (64 - sh)) : 0ull);
+      uint64_t vis = (lo >> sh) | (sh ? (static_cast<uint64_t>(wd[2]) << (64 - sh)) : 0ull);
+      if (jb < 0) vis |= (1ull << -jb) - 1;  // prefix keys of a straddling tile
+      // bit o of vis = key t0 + o visible; a lane's keys are o = 32 kb + 8 (v/4)
+      // + 4 h + v%4, so after dropping 4 h bits each test is a constant bit.
+      vis >>= 4 * h;
+      const uint32_t vw[2] = {static_cast<uint32_t>(vis), static_cast<uint32_t>(vis >> 32)};
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int v = 0; v < 16; ++v) {
-          const int o = kb * 32 + 8 * (v >> 2) + 4 * h + (v & 3);
-          const bool vis = (t0 + o < P) || ((win >> o) & 1ull);
-          if (!vis) sacc[kb][v] = -INFINITY;
-        }
+        for (int v = 0; v < 16; ++v)
+          if (!(vw[kb] & (1u << (8 * (v >> 2) + (v & 3))))) sacc[kb][v] = -INFINITY;
     }
-
-    // ---- online softmax (base 2, lazy rescale)
     float mx = -INFINITY;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -328,7 +355,6 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
       m_run = m_new;
     }
     const float base = (m_run == -INFINITY) ? 0.0f : m_run;
-    bf16x8 pf[4];
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -337,10 +363,12 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
         l_run += p;
         pf[kb * 2 + (v >> 3)][v & 7] = static_cast<__bf16>(p);
       }
+  };
 
-    // ---- O^T += V^T P^T; V^T fragments come from the row-major V tile through
-    // transposing LDS reads: in each 16-lane group, lane i gets 4 consecutive
-    // keys at head dim d0 + i when its 16 lanes point at (key k, dims 4q..4q+3).
+  // O^T += V^T P^T; V^T fragments come from the row-major V tile through
+  // transposing LDS reads: in each 16-lane group, lane i gets 4 consecutive
+  // keys at head dim d0 + i when its 16 lanes point at (key k, dims 4q..4q+3).
+  auto pv = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
@@ -361,20 +389,81 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
     }
   };
 
+  // matrix step i: O^T += V_{i-1}^T P_{i-1}^T (i >= 1) and S_i^T = K_i Q^T (i < nt)
+  auto matrix = [&](int i, int nt) __attribute__((always_inline)) {
+    if (i >= 1 && i < nt) {
+      pv((i - 1) & 1);
+      qk(i & 1);
+      // Keep the LDS reads three MFMAs ahead: 48 reads (32 transposing V
+      // reads, 16 K reads) feed 32 MFMAs.
+      __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
+#pragma unroll
+      for (int k = 0; k < 16; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+      }
+#pragma unroll
+      for (int k = 0; k < 10; ++k) {
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
+    } else if (i >= 1) {
+      pv((i - 1) & 1);
+    } else if (i < nt) {
+      qk(i & 1);
+    }
+  };
+
+  // Two wave groups in ping-pong: group 0 = waves 0-3, group 1 = waves 4-7,
+  // one wave of each per SIMD.  A wave's steps alternate: step 2i = matrix
+  // step i, step 2i+1 = softmax of tile i.  Group 0 runs step ph in phase ph,
+  // group 1 runs step ph-1, so within each pair of phases group 0 does
+  // [matrix i, softmax i] while group 1 does [softmax i-1, matrix i]: on every
+  // SIMD one wave's MFMAs overlap the other wave's exp/max/convert work.  The
+  // only barrier is at the end of each pair (one per tile), so the groups
+  // drift freely inside it.
+  // LDS: K_i -> k_lds[i & 1] and V_i -> v_lds[i & 1].  At the end of pair i
+  // every thread stores K_{i+1} and V_i (loaded into registers during pair
+  // i-1) and issues the loads of K_{i+2} and V_{i+1}.  Pair i reads only K_i
+  // and V_{i-1}, and a buffer is refilled a full pair after its last reader,
+  // with a barrier in between.
+  const int grp = w >> 2;
+  const bool active = rowbase + w * kRowsWave < rows;  // waves with no row skip the math
+  const int nt = te - tb;
+
   __syncthreads();  // page ids visible
-  // Iteration it computes tile it from LDS buffer (it - tb) & 1 while tile it+1
-  // is loading into registers; it is stored to the other buffer afterwards.
-  if (tb < te) {
-    fetch(tb * kKT);
-    stash(0);
+  if (nt > 0) {
+    page_ids(tb, pk);
+    fetch_k();
+    stash_k(0);
+    page_ids(tb + 1, pk);
+    page_ids(tb, pv_);
+    if (nt > 1) fetch_k();
+    fetch_v();
+    page_ids(tb + 2, pk);
+    page_ids(tb + 1, pv_);
   }
   __syncthreads();
-  for (int it = tb; it < te; ++it) {
-    const int buf = (it - tb) & 1;
-    if (it + 1 < te) fetch((it + 1) * kKT);
-    compute(buf, it * kKT);
-    if (it + 1 < te) stash(buf ^ 1);
-    __syncthreads();
+#pragma unroll 1
+  for (int ph = 0; ph < 2 * nt + 2; ++ph) {
+    const int j = ph - grp;  // this wave's step
+    if (active && j >= 0 && j <= 2 * nt) {
+      if ((j & 1) == 0)
+        matrix(j >> 1, nt);
+      else
+        softmax((tb + (j >> 1)) * kKT);
+    }
+    if (ph & 1) {
+      const int i = ph >> 1;
+      if (i + 1 < nt) stash_k((i + 1) & 1);
+      if (i < nt) stash_v(i & 1, (tb + i) * kKT);
+      if (i + 2 < nt) fetch_k();
+      if (i + 1 < nt) fetch_v();
+      page_ids(tb + i + 3, pk);
+      page_ids(tb + i + 2, pv_);
+      __syncthreads();
+    }
   }
 
   // ---- epilogue
