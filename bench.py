@@ -38,7 +38,59 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=3,
                     help="sequences of the workload the CPU oracle is timed on")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only copy BYTES device-to-device --steps times (a plain copy of known "
+                         "size, the reference that HBM byte counters are scaled by)")
     return ap.parse_args()
+
+
+ATTN_SRC = os.path.join(ROOT, "tree_causal_attention_amd", "csrc", "tree_attention.hip")
+PROFILES = os.path.join(ROOT, "profiles")
+
+
+def measured_traffic(workload):
+    """HBM bytes per jt_tree_attention launch from the committed counter summary.
+
+    The summary records the sha256 of the attention source it was measured on;
+    when the source has changed since, the figure no longer applies (None).
+    """
+    import hashlib
+    path = os.path.join(PROFILES, f"tree_attention_{workload}.md")
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as f:
+        for line in f:
+            if line.startswith("- ") and ":" in line:
+                k, v = line[2:].split(":", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    with open(ATTN_SRC, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    if fields.get("kernel source sha256") != sha:
+        return None
+    try:
+        return int(fields["HBM traffic per launch (bytes)"])
+    except (KeyError, ValueError):
+        return None
+
+
+def copy_probe(nbytes, steps):
+    import torch
+    a = torch.empty(nbytes, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    b.copy_(a)
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(steps):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    print(json.dumps({"copy_probe_bytes": nbytes, "ms_per_copy": ms,
+                      "GBps": 2 * nbytes / ms / 1e6}))
 
 
 def algorithmic_work(w, prefix, n_nodes, depth):
@@ -94,6 +146,9 @@ def main():
     if args.gpus != 1:
         print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
         sys.exit(2)
+    if args.copy_probe > 0:
+        copy_probe(args.copy_probe, args.steps)
+        return
     import numpy as np
     import torch
     from tree_causal_attention_amd import binding as B
@@ -188,13 +243,13 @@ def main():
             "tree_nodes_per_step": tokens,
         },
         "roofline": {
-            "kernel": "tree_attn_mfma (jt_tree_attention)",
+            "kernel": "jt_tree_attention (tree_attn_mfma + tree_attn_combine)",
             "bound": "mfma",
             "achieved": achieved_tflops,
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": achieved_tflops / PEAK_BF16_TFLOPS,
-            "traffic": None,
+            "traffic": measured_traffic(w.name),
             "algorithmic_flops": flops,
             "algorithmic_bytes": kv_bytes + qo_bytes,
         },
