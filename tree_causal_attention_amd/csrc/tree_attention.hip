@@ -48,6 +48,7 @@ constexpr int kWavesWG = 8;          // waves per workgroup (2 per SIMD)
 constexpr int kRowsWave = 32;        // query rows per wave
 constexpr int kRowsWG = kWavesWG * kRowsWave;
 constexpr int kAttnThreads = kWavesWG * kWave;
+constexpr int kStages = 4;           // K/V tile ring: a tile is fetched two pairs ahead
 constexpr int kMaxPagesLds = 4096;   // page ids staged per work item
 constexpr int kMaxTilesItem = kMaxPagesLds * kPage / kKT;
 constexpr int kXcds = 8;             // MI355X: 8 XCDs, workgroups dealt round-robin
@@ -57,6 +58,22 @@ constexpr float kRescaleThreshold = 8.0f;
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
+
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (LDS and export counters left unconstrained).
+constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
+// 16-byte chunk slot of logical chunk c of tile row `key` is c ^ swz<D>(key).
+// A K fragment read (16 lanes = 16 consecutive keys at one chunk) and a
+// transposing V read (16 lanes = 4 consecutive keys x 2 adjacent chunks) then
+// touch 16 distinct 16-byte bank groups.
+template <int D>
+__device__ __forceinline__ constexpr int swz(int key) {
+  if constexpr (D == 128)
+    return ((key & 7) << 1) | ((key >> 3) & 1);  // 256-byte rows: 16 slots per row
+  else
+    return (((key >> 1) & 3) << 1) | ((key >> 3) & 1);  // 128-byte rows: 2 rows per bank sweep
+}
 
 // Work decomposition (identical for every (sequence, KV head) group; a
 // group's actual row count and key range are read on the device):
@@ -142,18 +159,18 @@ __device__ __forceinline__ int part_row(const AttnArgs& a, int rt, int sp) {
 template <int D>
 __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   constexpr int CPK = D / 8;                 // 16-byte chunks per key row
-  constexpr int LPT = kKT * CPK / kAttnThreads;  // chunks per thread per tensor per tile
   constexpr int DB = D / 32;                 // 32-row blocks of O^T
   constexpr int KS = D / 16;                 // MFMA k-steps of K Q^T
+  constexpr int TE = kKT * D;                // elements of one K (or V) tile
+  constexpr int SB = 2 * TE * 2;             // bytes of one stage (K tile, then V tile)
+  constexpr int IPW = kKT * CPK / kWave / kWavesWG;  // DMA instructions per wave per tensor
+  static_assert(IPW * kWave * kWavesWG == kKT * CPK, "tile must split evenly over the waves");
+  static_assert(kPage % (kWave * IPW / CPK) == 0, "a wave's DMA share must stay in one page");
 
-  // Row strides padded by 16 B (K) and 32 B (V): the K fragment reads (32 keys
-  // at one 16-byte column) and the transposing V reads (4 keys x 32 bytes per
-  // 16 lanes) then spread over all banks, and every LDS address is a per-lane
-  // base plus a compile-time offset.
-  constexpr int KSTR = D + 8;
-  constexpr int VSTR = D + 16;
-  __shared__ __align__(16) uint16_t k_lds[2][kKT * KSTR];
-  __shared__ __align__(16) uint16_t v_lds[2][kKT * VSTR];
+  // Ring of kStages stage buffers (K tile, V tile); rows are unpadded and
+  // XOR-swizzled at 16-byte granularity (see swz), so each DMA instruction
+  // fills 1 KB of LDS contiguously.
+  __shared__ __align__(1024) uint16_t stages[kStages * 2 * TE];
   __shared__ __align__(16) int pg_lds[kMaxPagesLds];
 
   Item item;
@@ -175,11 +192,12 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   const int ntiles = (key_end + kKT - 1) / kKT;
   const int tb = static_cast<int>(static_cast<long long>(ntiles) * item.sp / item.splits);
   const int te = static_cast<int>(static_cast<long long>(ntiles) * (item.sp + 1) / item.splits);
+  const int nt = te - tb;
 
   // ---- page ids of this item's key range, staged in LDS (-1: no page)
   const int kv_len = P + n;
   const int pg0 = tb * (kKT / kPage);
-  const int nslots = (te - tb) * (kKT / kPage);
+  const int nslots = nt * (kKT / kPage);
   const int pg_end = (kv_len + kPage - 1) / kPage;
   {
     const int32_t* ptab = a.page_table + static_cast<size_t>(s) * a.max_pages;
@@ -220,9 +238,6 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   const uint16_t* kbase = a.k_pool + g * head_stride;
   const uint16_t* vbase = a.v_pool + g * head_stride;
 
-  // lane roles of the transposed V reads (groups of 16 lanes)
-  const int tg = lane >> 4, tk = (lane >> 2) & 3, tq = lane & 3;
-
   f32x16 o_acc[DB];
 #pragma unroll
   for (int db = 0; db < DB; ++db)
@@ -231,67 +246,91 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   float m_run = -INFINITY;  // running max in scaled (log2) units
   float l_run = 0.0f;       // this lane's half of the normaliser
 
-  // ---- global -> registers -> LDS.  Thread tid moves the 16-byte chunks
-  // (key tid / CPK + c * 512 / CPK, column tid % CPK) of a tile; the keys of
-  // one wave's chunk lie in one page, so the page base is wave-uniform (scalar
-  // registers) and each lane adds a fixed offset inside the page.
-  static_assert(LPT == 1 || LPT == 2, "staging is written for 1 or 2 chunks per thread");
-  static_assert(kPage % (kWave / CPK) == 0, "a wave's chunk must not straddle pages");
-  const int inner = ((tid / CPK) % kPage) * D + (tid % CPK) * 8;
-  // Page ids a wave needs for one tile (slot of chunk c inside the tile's 4
-  // pages), read from LDS one tile before the loads they address, so turning
-  // them into scalar bases never waits on LDS.
-  auto page_ids = [&](int tile, int (&pid)[LPT]) __attribute__((always_inline)) {
-    const int t = min(tile, te - 1) - tb;  // clamped: the last tile's ids stay in range
+  // ---- global -> LDS directly (global_load_lds_dwordx4).  Wave w fetches
+  // the chunks e = (w*IPW + i)*64 + lane of each tensor of a tile: tile row
+  // e / CPK at 16-byte slot e % CPK, which holds logical chunk slot ^ swz(row);
+  // a wave's rows lie in one page, so the page base is scalar.  The DMA is
+  // issued through inline assembly: the compiler then does not treat every
+  // LDS read as a possible reader of the stage in flight (it would wait for
+  // all DMAs before each read); the explicit waits and barriers below order
+  // the stages instead.
+  const uint16_t* zero = reinterpret_cast<const uint16_t*>(g_zero_page);
+  uint32_t dma_off[IPW];  // byte offset of the lane's chunk inside its page block
 #pragma unroll
-    for (int c = 0; c < LPT; ++c)
-      pid[c] = pg_lds[t * (kKT / kPage) + (w * (kWave / CPK) + c * (kAttnThreads / CPK)) / kPage];
+  for (int i = 0; i < IPW; ++i) {
+    const int e = (w * IPW + i) * kWave + lane;
+    const int key = e / CPK;
+    dma_off[i] = ((key % kPage) * D + ((e % CPK) ^ swz<D>(key)) * 8) * 2;
+  }
+  const int wu = __builtin_amdgcn_readfirstlane(w);       // wave index, scalar
+  const int wpage = (wu * IPW * kWave / CPK) / kPage;    // page slot of this wave's rows
+  const uint32_t lds0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>(
+      (__attribute__((address_space(3))) uint16_t*)stages));  // LDS byte offset
+  auto stage_of = [&](int ti) __attribute__((always_inline)) {
+    return static_cast<uint32_t>((ti & (kStages - 1)) * SB);
   };
-  auto chunk_ptr = [&](const uint16_t* base, int pid) __attribute__((always_inline)) {
-    const int p = __builtin_amdgcn_readfirstlane(pid);
-    const uint16_t* pb = (p >= 0) ? base + static_cast<size_t>(p) * page_stride
-                                  : reinterpret_cast<const uint16_t*>(g_zero_page);
-    return reinterpret_cast<const uint4*>(pb + inner);
+  auto page_of = [&](int ti) __attribute__((always_inline)) {
+    return (ti < nt) ? pg_lds[ti * (kKT / kPage) + wpage] : -1;
   };
-  uint4 kr0, kr1, vr0, vr1;
-  int pk[LPT], pv_[LPT];  // page ids of the next K and V loads
-  auto fetch_k = [&]() __attribute__((always_inline)) {
-    kr0 = *chunk_ptr(kbase, pk[0]);
-    if constexpr (LPT == 2) kr1 = *chunk_ptr(kbase, pk[1]);
-  };
-  auto fetch_v = [&]() __attribute__((always_inline)) {
-    vr0 = *chunk_ptr(vbase, pv_[0]);
-    if constexpr (LPT == 2) vr1 = *chunk_ptr(vbase, pv_[1]);
-  };
-  auto stash_k = [&](int buf) __attribute__((always_inline)) {
-    *reinterpret_cast<uint4*>(&k_lds[buf][(tid / CPK) * KSTR + (tid % CPK) * 8]) = kr0;
-    if constexpr (LPT == 2) {
-      const int e = tid + kAttnThreads;
-      *reinterpret_cast<uint4*>(&k_lds[buf][(e / CPK) * KSTR + (e % CPK) * 8]) = kr1;
-    }
+  // Issues tile ti's K and V (2*IPW instructions per wave).
+  auto issue = [&](int ti) __attribute__((always_inline)) {
+    const int pid = __builtin_amdgcn_readfirstlane(page_of(ti));
+    const uint16_t* kp = (pid >= 0) ? kbase + static_cast<size_t>(pid) * page_stride : zero;
+    const uint16_t* vp = (pid >= 0) ? vbase + static_cast<size_t>(pid) * page_stride : zero;
+    const uint32_t dst = lds0 + stage_of(ti) + wu * IPW * kWave * 16;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(dst + i * kWave * 16), "v"(dma_off[i]), "s"(kp) : "memory", "m0");
+#pragma unroll
+    for (int i = 0; i < IPW; ++i)
+      asm volatile("s_mov_b32 m0, %0\n\tglobal_load_lds_dwordx4 %1, %2"
+                   :: "s"(dst + TE * 2 + i * kWave * 16), "v"(dma_off[i]), "s"(vp)
+                   : "memory", "m0");
   };
   // Keys past the sequence inside its last page hold whatever the pool holds
-  // there: their scores are masked, and their V rows are zeroed here so a
+  // there: their scores are masked, and their V rows are zeroed here (each
+  // wave clears the chunks it fetched itself, after its own DMA landed) so a
   // zero weight never meets a non-finite value.
-  auto stash_v = [&](int buf, int t0) __attribute__((always_inline)) {
-    if (t0 + kKT > kv_len) {
-      const uint4 z = make_uint4(0, 0, 0, 0);
-      if (t0 + tid / CPK >= kv_len) vr0 = z;
-      if constexpr (LPT == 2)
-        if (t0 + (tid + kAttnThreads) / CPK >= kv_len) vr1 = z;
-    }
-    *reinterpret_cast<uint4*>(&v_lds[buf][(tid / CPK) * VSTR + (tid % CPK) * 8]) = vr0;
-    if constexpr (LPT == 2) {
-      const int e = tid + kAttnThreads;
-      *reinterpret_cast<uint4*>(&v_lds[buf][(e / CPK) * VSTR + (e % CPK) * 8]) = vr1;
+  auto clear_v_tail = [&](int ti) __attribute__((always_inline)) {
+    const int t0 = (tb + ti) * kKT;
+    if (t0 + kKT <= kv_len || ti >= nt) return;
+    uint16_t* vt = stages + (stage_of(ti) + TE * 2) / 2;
+#pragma unroll
+    for (int i = 0; i < IPW; ++i) {
+      const int e = (w * IPW + i) * kWave + lane;
+      if (t0 + e / CPK >= kv_len) *reinterpret_cast<uint4*>(vt + e * 8) = make_uint4(0, 0, 0, 0);
     }
   };
+  // LDS fragment addresses (bytes from the stage base): K fragment kk of a
+  // lane is kl ^ (kk << 5); V fragment (half hf, dims block db) is
+  // vl[hf] ^ (db << 6) -- XOR only touches the chunk slot bits.  Key block kb
+  // adds kb*32 rows, the 16-key step ks adds 16 rows.
+  const uint32_t kl = col * D * 2 + ((h ^ swz<D>(col)) << 4);
+  // transposing V reads: in each 16-lane group, lane (tk, tq) points at key
+  // 4h + tk (+8 for the upper half) and dims 32 db + 16 (tg&1) + 4 tq .. +3
+  const int tg = lane >> 4, tk = (lane >> 2) & 3, tq = lane & 3;
+  uint32_t vl[2];
+#pragma unroll
+  for (int hf = 0; hf < 2; ++hf) {
+    const int key = 4 * h + tk + 8 * hf;
+    vl[hf] = (TE + key * D) * 2 + (((2 * (tg & 1) + (tq >> 1)) ^ swz<D>(key)) << 4) + (tq & 1) * 8;
+  }
 
   f32x16 sacc[2];  // S^T of the tile between its QK and softmax phases
   bf16x8 pf[4];    // P^T of the tile between its softmax and PV phases
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) pf[k][e] = static_cast<__bf16>(0.0f);
 
   // S^T = K Q^T for 2 blocks of 32 keys (independent accumulators interleaved)
-  auto qk = [&](int buf) __attribute__((always_inline)) {
+  // (the stage base only has bits above the in-stage offset, so OR adds it;
+  // the sum is made opaque per call so the compiler derives the XORed
+  // fragment addresses here instead of keeping one register per fragment)
+  auto qk = [&](int ti) __attribute__((always_inline)) {
+    uint32_t kb_ = (lds0 + stage_of(ti)) | kl;
+    asm volatile("" : "+v"(kb_));
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -300,9 +339,8 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
     for (int kk = 0; kk < KS; ++kk) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const int key = kb * 32 + col;
-        const bf16x8 kf =
-            *reinterpret_cast<const bf16x8*>(&k_lds[buf][key * KSTR + 16 * kk + 8 * h]);
+        const bf16x8 kf = *reinterpret_cast<const bf16x8 __attribute__((address_space(3)))*>(
+            (kb_ ^ (kk << 5)) + kb * 32 * D * 2);
         sacc[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf, qreg[kk], sacc[kb], 0, 0, 0);
       }
     }
@@ -368,18 +406,17 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   // O^T += V^T P^T; V^T fragments come from the row-major V tile through
   // transposing LDS reads: in each 16-lane group, lane i gets 4 consecutive
   // keys at head dim d0 + i when its 16 lanes point at (key k, dims 4q..4q+3).
-  auto pv = [&](int buf) __attribute__((always_inline)) {
+  auto pv = [&](int ti) __attribute__((always_inline)) {
+    uint32_t v0 = (lds0 + stage_of(ti)) | vl[0], v1 = (lds0 + stage_of(ti)) | vl[1];
+    asm volatile("" : "+v"(v0), "+v"(v1));
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
 #pragma unroll
       for (int db = 0; db < DB; ++db) {
-        const int dst = 32 * db + 16 * (tg & 1) + 4 * tq;
-        const int ka = 16 * ks + 4 * h + tk;
-        const int kc = ka + 8;
         const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_ptr)(&v_lds[buf][ka * VSTR + dst]));
+            (lds_i16x4_ptr)((v0 ^ (db << 6)) + ks * 16 * D * 2));
         const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (lds_i16x4_ptr)(&v_lds[buf][kc * VSTR + dst]));
+            (lds_i16x4_ptr)((v1 ^ (db << 6)) + ks * 16 * D * 2));
         const uint2 ulo = __builtin_bit_cast(uint2, lo);
         const uint2 uhi = __builtin_bit_cast(uint2, hi);
         const uint4 u = make_uint4(ulo.x, ulo.y, uhi.x, uhi.y);
@@ -389,11 +426,14 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
     }
   };
 
-  // matrix step i: O^T += V_{i-1}^T P_{i-1}^T (i >= 1) and S_i^T = K_i Q^T (i < nt)
+  // matrix step i: O^T += V_{i-1}^T P_{i-1}^T and S_i^T = K_i Q^T.  Step 0's
+  // PV reads the zeroed V tile of stage -1 with P = 0, and step nt's QK reads
+  // the (zero-page) tile past the range, whose scores are never used: every
+  // step runs the same code.
   auto matrix = [&](int i, int nt) __attribute__((always_inline)) {
-    if (i >= 1 && i < nt) {
-      pv((i - 1) & 1);
-      qk(i & 1);
+    {
+      pv(i - 1);
+      qk(i);
       // Keep the LDS reads three MFMAs ahead: 48 reads (32 transposing V
       // reads, 16 K reads) feed 32 MFMAs.
       __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 6, 0);
@@ -408,10 +448,6 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
       }
       __builtin_amdgcn_sched_group_barrier(kSchedMfma, 6, 0);
-    } else if (i >= 1) {
-      pv((i - 1) & 1);
-    } else if (i < nt) {
-      qk(i & 1);
     }
   };
 
@@ -423,30 +459,33 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   // SIMD one wave's MFMAs overlap the other wave's exp/max/convert work.  The
   // only barrier is at the end of each pair (one per tile), so the groups
   // drift freely inside it.
-  // LDS: K_i -> k_lds[i & 1] and V_i -> v_lds[i & 1].  At the end of pair i
-  // every thread stores K_{i+1} and V_i (loaded into registers during pair
-  // i-1) and issues the loads of K_{i+2} and V_{i+1}.  Pair i reads only K_i
-  // and V_{i-1}, and a buffer is refilled a full pair after its last reader,
-  // with a barrier in between.
+  // LDS: tile t (K_t, V_t) lives in stage t % 4.  Pair i reads K_i and
+  // V_{i-1}, so tile t is read in pairs t and t+1.  At the start of pair i
+  // each wave issues the DMA of tile i+2 into the stage of tile i-2 (last read
+  // in pair i-1, before the barrier that closed it); at the end of pair i it
+  // waits until only that DMA is in flight, so tile i+1 is complete for every
+  // wave after the barrier.
   const int grp = w >> 2;
   const bool active = rowbase + w * kRowsWave < rows;  // waves with no row skip the math
-  const int nt = te - tb;
 
-  __syncthreads();  // page ids visible
+  {
+    // V tile of the stage read by step 0's PV (tile -1): zeros
+    uint4* vz = reinterpret_cast<uint4*>(stages + (stage_of(-1) + TE * 2) / 2);
+    for (int e = tid; e < TE / 8; e += kAttnThreads) vz[e] = make_uint4(0, 0, 0, 0);
+  }
+  __syncthreads();  // page ids and the zero tile visible
   if (nt > 0) {
-    page_ids(tb, pk);
-    fetch_k();
-    stash_k(0);
-    page_ids(tb + 1, pk);
-    page_ids(tb, pv_);
-    if (nt > 1) fetch_k();
-    fetch_v();
-    page_ids(tb + 2, pk);
-    page_ids(tb + 1, pv_);
+    issue(0);
+    issue(1);
+    __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPW));
+    asm volatile("" ::: "memory");
+    clear_v_tail(0);
+    asm volatile("" ::: "memory");
   }
   __syncthreads();
 #pragma unroll 1
   for (int ph = 0; ph < 2 * nt + 2; ++ph) {
+    if (!(ph & 1)) issue((ph >> 1) + 2);
     const int j = ph - grp;  // this wave's step
     if (active && j >= 0 && j <= 2 * nt) {
       if ((j & 1) == 0)
@@ -455,16 +494,16 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
         softmax((tb + (j >> 1)) * kKT);
     }
     if (ph & 1) {
-      const int i = ph >> 1;
-      if (i + 1 < nt) stash_k((i + 1) & 1);
-      if (i < nt) stash_v(i & 1, (tb + i) * kKT);
-      if (i + 2 < nt) fetch_k();
-      if (i + 1 < nt) fetch_v();
-      page_ids(tb + i + 3, pk);
-      page_ids(tb + i + 2, pv_);
-      __syncthreads();
+      __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPW));
+      asm volatile("" ::: "memory");
+      clear_v_tail((ph >> 1) + 1);
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_s_barrier();
+      asm volatile("" ::: "memory");
     }
   }
+  // drain the DMAs still in flight (tiles past the range) before exit
+  __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
 
   // ---- epilogue
   const float l_tot = l_run + __shfl_xor(l_run, 32, kWave);
