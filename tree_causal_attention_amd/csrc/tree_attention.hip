@@ -64,13 +64,17 @@ constexpr int kSchedDsRead = 0x100;
 constexpr int vmcnt_imm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 
 // 16-byte chunk slot of logical chunk c of tile row `key` is c ^ swz<D>(key).
-// A K fragment read (16 lanes = 16 consecutive keys at one chunk) and a
-// transposing V read (16 lanes = 4 consecutive keys x 2 adjacent chunks) then
-// touch 16 distinct 16-byte bank groups.
+// With 256-byte rows (D = 128) a row spans all 64 banks once, so the slot is
+// the bank group.  A K fragment read serves 16 lanes = 16 consecutive keys at
+// one chunk per cycle: swz is a bijection on key % 16.  A transposing V read
+// serves 32 lanes = 4 consecutive keys (4a..4a+3) x 4 consecutive chunks
+// (4b..4b+3) per cycle: bits 2-3 of swz are key % 4 (distinct per key) and
+// bits 0-1 do not depend on key % 4, so the 16 (key, chunk) pairs land on 16
+// distinct slots.
 template <int D>
 __device__ __forceinline__ constexpr int swz(int key) {
   if constexpr (D == 128)
-    return ((key & 7) << 1) | ((key >> 3) & 1);  // 256-byte rows: 16 slots per row
+    return ((key & 3) << 2) | ((key >> 2) & 3);
   else
     return (((key >> 1) & 3) << 1) | ((key >> 3) & 1);  // 128-byte rows: 2 rows per bank sweep
 }
