@@ -277,8 +277,12 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
     return (ti < nt) ? pg_lds[ti * (kKT / kPage) + wpage] : -1;
   };
   // Issues tile ti's K and V (2*IPW instructions per wave).
+  // The page id comes from a register read out of LDS one call earlier
+  // (pid_next), so issuing never waits on LDS.
+  int pid_next = -1;  // set once the page ids are visible
   auto issue = [&](int ti) __attribute__((always_inline)) {
-    const int pid = __builtin_amdgcn_readfirstlane(page_of(ti));
+    const int pid = __builtin_amdgcn_readfirstlane(pid_next);
+    pid_next = page_of(ti + 1);
     const uint16_t* kp = (pid >= 0) ? kbase + static_cast<size_t>(pid) * page_stride : zero;
     const uint16_t* vp = (pid >= 0) ? vbase + static_cast<size_t>(pid) * page_stride : zero;
     const uint32_t dst = lds0 + stage_of(ti) + wu * IPW * kWave * 16;
@@ -478,6 +482,7 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
     for (int e = tid; e < TE / 8; e += kAttnThreads) vz[e] = make_uint4(0, 0, 0, 0);
   }
   __syncthreads();  // page ids and the zero tile visible
+  pid_next = page_of(0);
   if (nt > 0) {
     issue(0);
     issue(1);
