@@ -1,12 +1,14 @@
 /*
  * jt.h -- C ABI of the tree speculative-decoding verify step on AMD MI355X
- * (gfx950).  Four operations, each a thin host entry point that validates its
+ * (gfx950).  Each operation is a thin host entry point that validates its
  * arguments and enqueues HIP kernels on the caller's stream:
  *
  *   jt_build_tree      candidate tree from the draft's per-depth logits
  *   jt_tree_meta       per-node ancestor bitmasks (the tree-causal mask)
  *   jt_tree_attention  paged tree-causal attention of every tree node
  *   jt_accept          greedy acceptance of the longest matching path
+ *   jt_accept_margin   acceptance under a probability-ratio margin
+ *   jt_commit_kv       move the accepted path's K/V next to the prefix
  *
  * Conventions shared by every call
  * --------------------------------
@@ -60,6 +62,9 @@ typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
 #define JT_DERR_BAD_PAGE 8    /* a page id outside [0, num_pages)                           */
 #define JT_DERR_BAD_PREFIX 16 /* prefix_len < 0, or prefix_len + n_nodes > pages * 16       */
 #define JT_DERR_BAD_DEPTH 32  /* depth[j] != depth[parent[j]] + 1, or deeper than depth_n   */
+#define JT_DERR_BAD_TOKEN 64  /* a token id outside [0, vocab)                              */
+#define JT_DERR_BAD_PATH 128  /* accept_len outside [0, depth_n], or accept_nodes not a     */
+                              /* strictly increasing list of node ids in [1, n_nodes)       */
 
 /* [host] Static, NUL-terminated description of a status code. */
 const char* jt_status_string(jt_status s);
@@ -215,6 +220,68 @@ jt_status jt_accept(const void* target_logits, jt_dtype dt, int batch, int max_n
                     const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
                     int32_t* accept_nodes, int32_t* bonus_token, int32_t* err, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * jt_accept_margin -- acceptance under the per-step margin rule.
+ *
+ * AdaptiveSpec page (kongchang.com, "AdaptiveSpec：免训练推测解码方案提速56%的
+ * 技术解析"), section on the per-step margin rule: a drafted token is kept when
+ * the target's probability of it divided by the target's top-1 probability
+ * reaches a threshold theta, even when it is not the top-1 token (the page's
+ * example keeps a token at 0.30 against a top-1 at 0.35 with theta = 0.8).
+ * With p = softmax(L / T) that ratio is exp((L[x] - max L) / T), so the rule is
+ * L[x] - max L >= logit_margin with logit_margin = T * ln(theta).
+ *
+ * Same arguments, outputs and walk as jt_accept, except the per-node test:
+ * node v >= 1 is accepted iff its parent is accepted and
+ *   (double)L[parent(v)][token[v]] - (double)max_x L[parent(v)][x] >= logit_margin
+ * evaluated in fp64 on the stored logit values.  Several siblings may pass;
+ * the path ends at the deepest accepted node (lowest index among equals) and
+ * bonus_token is the argmax (lowest id) of that node's row.
+ *   logit_margin  finite and <= 0 (0 keeps only tokens tied with the maximum).
+ *   err           as jt_accept, plus JT_DERR_BAD_TOKEN (a token id outside
+ *                 [0, vocab): that sequence's outputs are then zero / -1).
+ * ---------------------------------------------------------------------- */
+jt_status jt_accept_margin(const void* target_logits, jt_dtype dt, int batch, int max_nodes,
+                           int vocab, int depth_n, const int32_t* parent, const int32_t* token,
+                           const int32_t* depth, const int32_t* n_nodes, double logit_margin,
+                           int32_t* accept_len, int32_t* accept_nodes, int32_t* bonus_token,
+                           int32_t* err, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * jt_commit_kv -- commit the accepted path to the KV cache.
+ *
+ * After acceptance the next decode step starts from the accepted state
+ * (JetSpec news piece, mlqm.cn/news/158889, tree-construction paragraph).
+ * With the tree tail at positions P + j (jt_tree_attention), the k-th accepted
+ * node a_k (k = 1..accept_len, depth order, as jt_accept writes them) moves
+ * from position P + a_k to P + k in every KV head of both pools; the root
+ * (position P) and positions past P + accept_len are not written; then
+ * prefix_len += 1 + accept_len (root plus accepted nodes).  All source rows of
+ * a sequence are read before any row is written, so overlapping sources and
+ * destinations are fine.  Afterwards, decode attention of node a_L over the
+ * new prefix equals its tree attention before the commit.
+ *
+ *   k_pool, v_pool  [num_pages, num_kv_heads, page_size, head_dim]  dt (in/out).
+ *   page_table      [batch, max_pages_per_seq] int32 (as jt_tree_attention).
+ *                   Tail pages must not be shared between sequences.
+ *   n_nodes         [batch] int32 (the tree's node count).
+ *   accept_len      [batch] int32; accept_nodes [batch, depth_n] int32 (as
+ *                   from jt_accept / jt_accept_margin).
+ *   prefix_len      [batch] int32 (in/out).
+ *   err             JT_DERR_BAD_PATH (accept_len outside [0, min(depth_n,
+ *                   n_nodes - 1)], accept_nodes not strictly increasing in
+ *                   [1, n_nodes), n_nodes or prefix_len invalid), JT_DERR_BAD_PAGE;
+ *                   such a sequence is left unchanged.
+ * Limits: page_size == 16, head_dim * element size a multiple of 16 bytes,
+ * 1 <= depth_n <= 64 with 2 * depth_n * head_dim * element size <= 64 KiB,
+ * 1 <= max_nodes <= 1024.
+ * ---------------------------------------------------------------------- */
+jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int num_kv_heads,
+                       int head_dim, const int32_t* page_table, int max_pages_per_seq,
+                       int num_pages, int page_size, const int32_t* n_nodes, int max_nodes,
+                       int depth_n, const int32_t* accept_len, const int32_t* accept_nodes,
+                       int32_t* prefix_len, int32_t* err, void* stream);
 
 #ifdef __cplusplus
 }

@@ -397,3 +397,108 @@ def accept(target_logits, parent, token, depth, n_nodes, n_depth):
     nodes = np.full(n_depth, -1, dtype=np.int64)
     nodes[:len(path)] = path
     return int(depth[best]), nodes, int(a[best])
+
+
+# ---------------------------------------------------------------------------
+# f3: margin acceptance (AdaptiveSpec's per-step margin rule)
+# ---------------------------------------------------------------------------
+
+def accept_margin(target_logits, parent, token, depth, n_nodes, n_depth, logit_margin):
+    """Margin acceptance of one sequence.
+
+    AdaptiveSpec page (kongchang.com, "AdaptiveSpec：免训练推测解码方案提速56%的
+    技术解析"), section on the per-step margin rule: a drafted token is kept
+    when the target's probability of it, divided by the target's top-1
+    probability, reaches a threshold theta, even if it is not the top-1 token.
+    With p = softmax(L / T) the ratio is exp((L[x] - max L) / T), so the test
+    is L[x] - max L >= T ln(theta) =: logit_margin (<= 0).
+
+    Reading: the test is evaluated in fp64 on the stored logits (fp32 or bf16
+    values, exact in fp64); the root is accepted; node v >= 1 is accepted when
+    its parent is accepted and its token passes the test on the parent's row;
+    the path ends at the deepest accepted node (lowest index among equals); the
+    bonus token is the argmax (lowest id) of the end node's row.  With
+    logit_margin = 0 only tokens tied with the maximum pass.
+    Returns (accept_len, accept_nodes [n_depth], bonus_token).
+    """
+    X = np.asarray(target_logits)[:n_nodes].astype(np.float64)
+    if np.isnan(X).any():
+        raise OracleInputError("target logits must not be NaN")
+    if not (logit_margin <= 0.0 and np.isfinite(logit_margin)):
+        raise OracleInputError("logit_margin must be finite and <= 0")
+    top = X.max(axis=1)
+    a = np.argmax(X, axis=1)
+    acc = [False] * n_nodes
+    acc[0] = True
+    for v in range(1, n_nodes):
+        p = int(parent[v])
+        acc[v] = acc[p] and (X[p, int(token[v])] - top[p] >= logit_margin)
+    best = 0
+    for v in range(1, n_nodes):
+        if acc[v] and depth[v] > depth[best]:
+            best = v
+    path = ancestors(parent, best)[1:]
+    nodes = np.full(n_depth, -1, dtype=np.int64)
+    nodes[:len(path)] = path
+    return int(depth[best]), nodes, int(a[best])
+
+
+def margin_from_ratio(theta, temperature=1.0):
+    """logit_margin = T ln(theta) for a probability-ratio threshold theta in (0, 1]."""
+    import math
+    return float(temperature) * math.log(float(theta))
+
+
+# ---------------------------------------------------------------------------
+# f1: committing the accepted path to the KV cache
+# ---------------------------------------------------------------------------
+
+def commit_kv(k_pool, v_pool, page_table_row, prefix_len, accept_len, accept_nodes):
+    """KV commit of one sequence after acceptance (returns new pools and prefix).
+
+    Follows from where the tree tail lives (node j at logical position P + j,
+    design reading R10) and from the step the JetSpec news piece describes
+    next: the next decode step starts from the state the verification accepted.
+    The root (node 0, position P) stays; the k-th accepted node a_k
+    (k = 1..L, depth order) moves from position P + a_k to P + k; positions
+    past P + L are left as they are; the new prefix length is P + 1 + L.
+    All source rows are read before any row is written.
+    """
+    k_pool = np.array(k_pool, copy=True)
+    v_pool = np.array(v_pool, copy=True)
+    P = int(prefix_len)
+    L = int(accept_len)
+    table = np.asarray(page_table_row)
+    src = [P + int(accept_nodes[k]) for k in range(L)]
+    rows_k = [k_pool[table[t // PAGE_SIZE], :, t % PAGE_SIZE, :].copy() for t in src]
+    rows_v = [v_pool[table[t // PAGE_SIZE], :, t % PAGE_SIZE, :].copy() for t in src]
+    for k in range(L):
+        t = P + 1 + k
+        k_pool[table[t // PAGE_SIZE], :, t % PAGE_SIZE, :] = rows_k[k]
+        v_pool[table[t // PAGE_SIZE], :, t % PAGE_SIZE, :] = rows_v[k]
+    return k_pool, v_pool, P + 1 + L
+
+
+def decode_attention(q, k_pool, v_pool, page_table_row, length, scale):
+    """Plain decode attention of one query over logical positions 0..length-1.
+
+    q: [Hq, D].  Returns (o [Hq, D], lse [Hq]) in fp64: s = scale * q.k over
+    every key, o = softmax(s) @ v, lse = log sum exp(s).
+    """
+    q = np.asarray(q)
+    Hq = q.shape[0]
+    Hkv = np.asarray(k_pool).shape[1]
+    group = Hq // Hkv
+    K = gather_kv(k_pool, page_table_row, length)
+    V = gather_kv(v_pool, page_table_row, length)
+    o = np.empty((Hq, q.shape[1]))
+    lse = np.empty(Hq)
+    for h in range(Hq):
+        g = h // group
+        s = scale * (K[g] @ q[h].astype(np.float64))
+        m = s.max()
+        e = np.exp(s - m)
+        z = e.sum()
+        o[h] = (e @ V[g]) / z
+        lse[h] = m + np.log(z)
+    return o, lse

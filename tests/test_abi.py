@@ -120,3 +120,34 @@ def test_workspace_queries_are_consistent(lib):
     b = lib.jt_accept_workspace(8, 257, 151936)
     assert 0 < a <= b
     assert lib.jt_tree_attention_workspace(1, 17, 4, 1, 64, 8, 16, 0) == 0   # fp32: no split
+
+
+def test_accept_margin_validation(lib):
+    f = lib.jt_accept_margin
+    p = ctypes.c_void_p(1)
+
+    def call(margin=-0.5, dt=0, b=1, T=17, V=100, N=4, ws=0):
+        return f(p, dt, b, T, V, N, p, p, p, p, margin, p, p, p, None, p, ws, None)
+
+    assert call(margin=0.1) == B.JT_ERR_INVALID_ARG           # a ratio above 1
+    assert call(margin=float("nan")) == B.JT_ERR_INVALID_ARG
+    assert call(margin=float("-inf")) == B.JT_ERR_INVALID_ARG
+    assert call(N=0) == B.JT_ERR_INVALID_ARG
+    assert call(T=1025) == B.JT_ERR_UNSUPPORTED
+    assert call(ws=0) == B.JT_ERR_WORKSPACE
+    assert call(b=0) == B.JT_OK
+
+
+def test_commit_kv_validation(lib):
+    f = lib.jt_commit_kv
+    p = ctypes.c_void_p(1)
+
+    def call(dt=1, b=1, hkv=2, D=128, maxp=4, npages=8, ps=16, T=17, N=16):
+        return f(p, p, dt, b, hkv, D, p, maxp, npages, ps, p, T, N, p, p, p, None, None)
+
+    assert call(ps=32) == B.JT_ERR_UNSUPPORTED
+    assert call(D=4) == B.JT_ERR_UNSUPPORTED        # 8-byte rows
+    assert call(N=65) == B.JT_ERR_UNSUPPORTED
+    assert call(hkv=0) == B.JT_ERR_INVALID_ARG
+    assert call(dt=3) == B.JT_ERR_INVALID_ARG
+    assert call(b=0) == B.JT_OK

@@ -1,0 +1,277 @@
+"""GPU parity of the margin acceptance (jt_accept_margin) and the KV commit
+(jt_commit_kv) against the CPU oracle: bit-exact integer outputs and bit-exact
+committed pools."""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import tree_oracle as O
+from tree_causal_attention_amd import binding as B
+from tree_causal_attention_amd import workloads as WL
+
+from gpu_util import check_attention, dev, to_np
+
+pytestmark = pytest.mark.gpu
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _say(msg):
+    print(msg, flush=True)
+
+
+def _tree(rng, n):
+    par = [-1] + [int(rng.integers(0, v)) for v in range(1, n)]
+    dep = [0] * n
+    for v in range(1, n):
+        dep[v] = dep[par[v]] + 1
+    return par, dep
+
+
+def _pad(rows, T, fill=-1):
+    return [list(r) + [fill] * (T - len(r)) for r in rows]
+
+
+def _gpu_margin(X, N, parents, tokens, depths, ns, margin):
+    d = dev()
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    i32 = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.int32).to(d)
+    alen, anodes, bonus = B.jt_accept_margin(X.to(d), N, i32(parents), i32(tokens), i32(depths),
+                                             i32(ns), margin, err=err)
+    torch.cuda.synchronize()
+    return to_np(alen), to_np(anodes), to_np(bonus), int(err.item())
+
+
+# ------------------------------------------------------------ margin accept
+
+def test_margin_page_example_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "margin_example.json")))
+    X = torch.from_numpy(np.log(np.array(g["target_probs"], dtype=np.float64)).astype(np.float32))
+    for c in g["cases"]:
+        m = B.margin_from_ratio(c["theta"])
+        alen, anodes, bonus, err = _gpu_margin(X[None], 1, [g["parent"]], [g["token"]],
+                                               [g["depth"]], [2], m)
+        assert err == 0
+        # the float32 logits must give the same decisions as the page's ratios
+        L, nodes, bb = O.accept_margin(X.numpy(), g["parent"], g["token"], g["depth"], 2, 1, m)
+        assert (L, nodes.tolist(), bb) == (c["accept_len"], c["accept_nodes"], c["bonus"])
+        assert (int(alen[0]), anodes[0].tolist(), int(bonus[0])) == (L, nodes.tolist(), bb)
+
+
+@pytest.mark.parametrize("seed,dtype", [(s, dt) for s in range(6) for dt in ("f32", "bf16")])
+def test_margin_small_random_trees(seed, dtype):
+    """Coarse logits make ties and several passing siblings common."""
+    rng = np.random.default_rng(500 + seed)
+    b, T, V, N = 4, 60, 16, 64
+    pars, deps, toks, ns = [], [], [], []
+    for s in range(b):
+        n = int(rng.integers(1, T + 1))
+        p, dd = _tree(rng, n)
+        pars.append(p)
+        deps.append(dd)
+        toks.append([int(x) for x in rng.integers(0, V, n)])
+        ns.append(n)
+    X = torch.from_numpy(np.round(rng.standard_normal((b, T, V)) * 2, 1).astype(np.float32))
+    if dtype == "bf16":
+        X = X.to(torch.bfloat16)
+    margin = -float(rng.uniform(0.0, 2.5))
+    alen, anodes, bonus, err = _gpu_margin(X, N, _pad(pars, T), _pad(toks, T, 0), _pad(deps, T),
+                                           ns, margin)
+    assert err == 0
+    Xf = X.float().numpy()
+    for s in range(b):
+        L, nodes, bb = O.accept_margin(Xf[s], pars[s], toks[s], deps[s], ns[s], N, margin)
+        assert (int(alen[s]), int(bonus[s])) == (L, bb), f"seq {s}"
+        assert np.array_equal(anodes[s], nodes), f"seq {s}"
+
+
+def test_margin_workload_planted(oracle_trees_extras):
+    """The B=256 tree and [257, 151936] target rows: a planted path plus a
+    near-top sibling at every level, so the margin rule keeps more than greedy."""
+    name, inst = "qwen3_8b_b256", 0
+    w = WL.WORKLOADS[name]
+    x = WL.make_inputs(w, inst)
+    t = oracle_trees_extras(name, inst, x, w)[0]
+    tgt = x.target[0].clone()
+    n = t["n_nodes"]
+    deepest = int(np.argmax(t["depth"][:n]))
+    WL.plant_path(tgt, t["parent"], t["token"], deepest)
+    rng = np.random.default_rng(7)
+    on_path = set(O.ancestors(t["parent"], deepest))
+    for v in rng.integers(1, n, 40):  # off-path nodes close to their parent's maximum
+        if int(v) in on_path:
+            continue
+        p = int(t["parent"][v])
+        tgt[p, int(t["token"][v])] = tgt[p].max() - 0.5
+    par, tok, dep = t["parent"], t["token"], t["depth"]
+    for theta in (0.9, 0.5, 0.3):
+        m = B.margin_from_ratio(theta)
+        alen, anodes, bonus, err = _gpu_margin(tgt[None], w.depth_n, [par], [tok], [dep], [n], m)
+        assert err == 0
+        L, nodes, bb = O.accept_margin(tgt.numpy(), par, tok, dep, n, w.depth_n, m)
+        assert (int(alen[0]), int(bonus[0])) == (L, bb), theta
+        assert np.array_equal(anodes[0], nodes)
+        assert L >= int(t["depth"][deepest])
+
+
+def test_margin_rejects_bad_token():
+    X = torch.zeros((1, 3, 8))
+    alen, anodes, bonus, err = _gpu_margin(X, 2, [[-1, 0, 1]], [[0, 9, 1]], [[0, 1, 2]], [3], -1.0)
+    assert err & B.DERR_BAD_TOKEN
+    assert int(alen[0]) == 0 and (anodes[0] == -1).all()
+
+
+@pytest.fixture(scope="module")
+def oracle_trees_extras():
+    cache = {}
+
+    def get(name, inst, x, w):
+        key = (name, inst)
+        if key not in cache:
+            cache[key] = [O.build_tree(x.draft[s].numpy(), w.width_w, w.budget_b,
+                                       int(x.root_token[s]), check_exact=False)
+                          for s in range(w.batch)]
+        return cache[key]
+    return get
+
+
+# ---------------------------------------------------------------- KV commit
+
+def _commit_case(rng, b, hkv, D, dtype, T=40, N=16):
+    pages_per = []
+    prefixes, ns, pars, deps, paths = [], [], [], [], []
+    for s in range(b):
+        n = int(rng.integers(1, T + 1))
+        p, dd = _tree(rng, n)
+        P = int(rng.integers(0, 70))
+        end = int(rng.integers(0, n))
+        path = O.ancestors(p, end)[1:][:N]
+        prefixes.append(P)
+        ns.append(n)
+        pars.append(p)
+        deps.append(dd)
+        paths.append(path)
+        pages_per.append((P + n + 15) // 16 + int(rng.integers(0, 2)))
+    total = sum(pages_per) + 2
+    perm = rng.permutation(total)
+    maxp = max(pages_per)
+    table = np.full((b, maxp), -1, dtype=np.int32)
+    off = 0
+    for s in range(b):
+        table[s, :pages_per[s]] = perm[off:off + pages_per[s]]
+        off += pages_per[s]
+    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    k = torch.randn((total, hkv, 16, D), generator=torch.Generator().manual_seed(int(rng.integers(1 << 30)))).to(tdt)
+    v = torch.randn((total, hkv, 16, D), generator=torch.Generator().manual_seed(int(rng.integers(1 << 30)))).to(tdt)
+    alen = np.array([len(pth) for pth in paths], dtype=np.int32)
+    anodes = np.full((b, N), -1, dtype=np.int32)
+    for s in range(b):
+        anodes[s, :alen[s]] = paths[s]
+    return dict(k=k, v=v, table=table, total=total, P=np.array(prefixes, dtype=np.int32),
+                n=np.array(ns, dtype=np.int32), alen=alen, anodes=anodes, T=T, N=N)
+
+
+def _bits(t):
+    """The pool as raw bit patterns (the commit only moves bytes)."""
+    return (t.view(torch.int16) if t.dtype == torch.bfloat16 else t).numpy()
+
+
+def _oracle_commit(c, seqs):
+    kr, vr = _bits(c["k"]), _bits(c["v"])
+    Ps = {}
+    for s in seqs:
+        kr, vr, Ps[s] = O.commit_kv(kr, vr, c["table"][s], int(c["P"][s]), int(c["alen"][s]),
+                                    c["anodes"][s])
+    return kr, vr, Ps
+
+
+def _gpu_commit(c, err_expected=0):
+    d = dev()
+    k, v = c["k"].to(d), c["v"].to(d)
+    P = torch.from_numpy(c["P"].copy()).to(d)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    B.jt_commit_kv(k, v, torch.from_numpy(c["table"]).to(d), c["total"],
+                   torch.from_numpy(c["n"]).to(d), c["T"], torch.from_numpy(c["alen"]).to(d),
+                   torch.from_numpy(c["anodes"]).to(d), P, err=err)
+    torch.cuda.synchronize()
+    return k.cpu(), v.cpu(), P.cpu().numpy(), int(err.item())
+
+
+@pytest.mark.parametrize("seed,hkv,D,dtype", [(0, 1, 64, "f32"), (1, 4, 128, "bf16"),
+                                             (2, 8, 128, "bf16"), (3, 2, 64, "bf16"),
+                                             (4, 3, 128, "f32")])
+def test_commit_bit_exact(seed, hkv, D, dtype):
+    rng = np.random.default_rng(700 + seed)
+    c = _commit_case(rng, 6, hkv, D, dtype)
+    _say(f"commit seed {seed} hkv {hkv} D {D} {dtype}")
+    kg, vg, Pg, err = _gpu_commit(c)
+    assert err == 0
+    kr, vr, Ps = _oracle_commit(c, range(len(c["P"])))
+    for s, P2 in Ps.items():
+        assert int(Pg[s]) == P2
+    assert np.array_equal(_bits(kg), kr) and np.array_equal(_bits(vg), vr)
+
+
+def test_commit_rejects_bad_path_and_leaves_it():
+    rng = np.random.default_rng(9)
+    c = _commit_case(rng, 3, 2, 64, "bf16")
+    c["n"][1] = max(int(c["n"][1]), 4)
+    c["alen"][1] = 2
+    c["anodes"][1, :2] = [3, 2]  # not increasing
+    kg, vg, Pg, err = _gpu_commit(c)
+    assert err & B.DERR_BAD_PATH
+    assert int(Pg[1]) == int(c["P"][1])
+    # the other sequences are committed as usual
+    kr, vr, Ps = _oracle_commit(c, (0, 2))
+    for s, P2 in Ps.items():
+        assert int(Pg[s]) == P2
+    assert np.array_equal(_bits(kg), kr) and np.array_equal(_bits(vg), vr)
+
+
+def test_commit_then_decode_matches_tree_attention():
+    """On the GPU: tree attention of the last accepted node before the commit
+    equals single-node attention at the new prefix after it."""
+    rng = np.random.default_rng(11)
+    b, hq, hkv, D, T = 3, 8, 2, 128, 40
+    c = _commit_case(rng, b, hkv, D, "bf16", T=T)
+    d = dev()
+    q = torch.randn((b, T, hq, D), generator=torch.Generator().manual_seed(5)).to(torch.bfloat16)
+    par = np.full((b, T), -1, dtype=np.int32)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    # rebuild each sequence's tree from its path so that the path is valid:
+    # a chain through the accepted nodes, everything else hanging off the root
+    for s in range(b):
+        n = int(c["n"][s])
+        par[s, :n] = 0
+        par[s, 0] = -1
+        prev = 0
+        for u in c["anodes"][s][:c["alen"][s]]:
+            par[s, u] = prev
+            prev = u
+    n_t = torch.from_numpy(c["n"]).to(d)
+    anc = B.jt_tree_meta(torch.from_numpy(par).to(d), n_t, err=err)
+    k, v = c["k"].to(d), c["v"].to(d)
+    table = torch.from_numpy(c["table"]).to(d)
+    o_tree, _ = B.jt_tree_attention(q.to(d), k, v, n_t, torch.from_numpy(c["P"]).to(d), table,
+                                    c["total"], anc, 0.1, err=err)
+    P = torch.from_numpy(c["P"].copy()).to(d)
+    B.jt_commit_kv(k, v, table, c["total"], n_t, T, torch.from_numpy(c["alen"]).to(d),
+                   torch.from_numpy(c["anodes"]).to(d), P, err=err)
+    # single-node trees whose node 0 is the last committed row (position P_new - 1)
+    one = torch.ones(b, dtype=torch.int32, device=d)
+    par1 = torch.full((b, T), -1, dtype=torch.int32, device=d)
+    anc1 = B.jt_tree_meta(par1, one, err=err)
+    q1 = torch.zeros_like(q)
+    for s in range(b):
+        end = int(c["anodes"][s][c["alen"][s] - 1]) if c["alen"][s] > 0 else 0
+        q1[s, 0] = q[s, end]
+    o_dec, _ = B.jt_tree_attention(q1.to(d), k, v, one, P - 1, table, c["total"], anc1, 0.1,
+                                   err=err)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for s in range(b):
+        end = int(c["anodes"][s][c["alen"][s] - 1]) if c["alen"][s] > 0 else 0
+        check_attention(o_dec[s, 0].double().cpu().numpy(), o_tree[s, end].double().cpu().numpy(),
+                        "bf16", f"seq {s}")

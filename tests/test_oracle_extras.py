@@ -1,0 +1,150 @@
+"""Pins for the oracle's margin acceptance and KV commit.
+
+Margin acceptance: the page's worked example (tests/golden), reduction to
+greedy acceptance at a zero margin when rows have no ties, path enumeration
+with Python's own arithmetic, and monotonicity in the threshold.
+
+KV commit: element-by-element positions against the definition, a path whose
+sources overlap later destinations, and the invariance that makes the commit
+correct: after it, plain decode attention of the last accepted node over the
+new prefix equals that node's tree attention before it.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+
+from oracle import tree_oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# --------------------------------------------------------------- margin rule
+
+def test_margin_page_example():
+    g = json.load(open(os.path.join(GOLDEN, "margin_example.json")))
+    X = np.log(np.array(g["target_probs"], dtype=np.float64))
+    for c in g["cases"]:
+        L, nodes, bonus = O.accept_margin(X, g["parent"], g["token"], g["depth"], 2, 1,
+                                          O.margin_from_ratio(c["theta"]))
+        assert L == c["accept_len"], c
+        assert nodes.tolist() == c["accept_nodes"], c
+        assert bonus == c["bonus"], c
+
+
+def _tree(rng, n):
+    par = [-1] + [int(rng.integers(0, v)) for v in range(1, n)]
+    dep = [0] * n
+    for v in range(1, n):
+        dep[v] = dep[par[v]] + 1
+    return par, dep
+
+
+@pytest.mark.parametrize("seed", range(20))
+def test_margin_zero_is_greedy_without_ties(seed):
+    rng = np.random.default_rng(seed)
+    n, V = int(rng.integers(1, 40)), 50
+    par, dep = _tree(rng, n)
+    X = rng.standard_normal((n, V)).astype(np.float32)  # continuous: no ties
+    a = X.argmax(axis=1)
+    tok = [0] + [int(a[par[v]]) if rng.random() < 0.6 else int(rng.integers(0, V))
+                 for v in range(1, n)]
+    got = O.accept_margin(X, par, tok, dep, n, max(dep) + 1, 0.0)
+    ref = O.accept(X, par, tok, dep, n, max(dep) + 1)
+    assert got[0] == ref[0] and got[2] == ref[2]
+    assert np.array_equal(got[1], ref[1])
+
+
+def _brute_margin(X, par, tok, dep, n, margin):
+    rows = [[float(x) for x in X[r]] for r in range(n)]
+    top = [max(r) for r in rows]
+    best, best_d = 0, 0
+    for v in range(n):
+        path, u = [], v
+        while u > 0:
+            path.append(u)
+            u = par[u]
+        if all(rows[par[u]][tok[u]] - top[par[u]] >= margin for u in path):
+            if len(path) > best_d:
+                best, best_d = v, len(path)
+    path, u = [], best
+    while u > 0:
+        path.append(u)
+        u = par[u]
+    bonus = max(range(len(rows[best])), key=lambda t: (rows[best][t], -t))
+    return best_d, path[::-1], bonus
+
+
+@pytest.mark.parametrize("seed", range(30))
+def test_margin_matches_path_enumeration(seed):
+    rng = np.random.default_rng(100 + seed)
+    n, V = int(rng.integers(1, 30)), 12
+    par, dep = _tree(rng, n)
+    X = np.round(rng.standard_normal((n, V)) * 2, 1).astype(np.float32)  # coarse: ties happen
+    tok = [0] + [int(rng.integers(0, V)) for _ in range(1, n)]
+    margin = -float(rng.uniform(0.0, 3.0))
+    L, nodes, bonus = O.accept_margin(X, par, tok, dep, n, max(dep) + 1, margin)
+    bL, bpath, bb = _brute_margin(X, par, tok, dep, n, margin)
+    assert L == bL and bonus == bb
+    assert nodes[:L].tolist() == bpath and (nodes[L:] == -1).all()
+
+
+@pytest.mark.parametrize("seed", range(10))
+def test_margin_monotone_in_threshold(seed):
+    rng = np.random.default_rng(200 + seed)
+    n, V = 40, 16
+    par, dep = _tree(rng, n)
+    X = rng.standard_normal((n, V)).astype(np.float32)
+    tok = [0] + [int(rng.integers(0, V)) for _ in range(1, n)]
+    lens = [O.accept_margin(X, par, tok, dep, n, max(dep) + 1, O.margin_from_ratio(t))[0]
+            for t in (1.0, 0.8, 0.5, 0.2, 0.05)]
+    assert lens == sorted(lens)
+
+
+# ----------------------------------------------------------------- KV commit
+
+def _pool(rng, pages, hkv, d):
+    return rng.standard_normal((pages, hkv, 16, d))
+
+
+@pytest.mark.parametrize("P,nodes", [(5, [1, 2, 3]), (16, [2, 3, 5]), (31, [4]), (0, []),
+                                     (20, [1, 5, 6, 9, 12])])
+def test_commit_positions(P, nodes):
+    rng = np.random.default_rng(P)
+    hkv, d, npages = 2, 8, 8
+    k, v = _pool(rng, npages, hkv, d), _pool(rng, npages, hkv, d)
+    table = rng.permutation(npages)
+    L = len(nodes)
+    k2, v2, P2 = O.commit_kv(k, v, table, P, L, nodes)
+    assert P2 == P + 1 + L
+
+    def row(pool, t):
+        return pool[table[t // 16], :, t % 16, :]
+    for t in range(npages * 16):
+        if P + 1 <= t <= P + L:
+            src = P + nodes[t - P - 1]
+            assert np.array_equal(row(k2, t), row(k, src)) and np.array_equal(row(v2, t), row(v, src))
+        else:
+            assert np.array_equal(row(k2, t), row(k, t)) and np.array_equal(row(v2, t), row(v, t))
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_commit_then_decode_equals_tree_attention(seed):
+    rng = np.random.default_rng(300 + seed)
+    hq, hkv, d = 4, 2, 16
+    n = 12
+    par, dep = _tree(rng, n)
+    P = int(rng.integers(0, 40))
+    npages = (P + n + 15) // 16 + 1
+    k, v = _pool(rng, npages, hkv, d), _pool(rng, npages, hkv, d)
+    table = rng.permutation(npages)
+    q = rng.standard_normal((n, hq, d))
+    end = int(rng.integers(1, n))
+    path = O.ancestors(par, end)[1:]  # accepted nodes, root excluded
+    o_tree, l_tree = O.tree_attention_seq(q, k, v, table, P, par, n, 0.25, nodes=[end])
+    k2, v2, P2 = O.commit_kv(k, v, table, P, len(path), path)
+    o_dec, l_dec = O.decode_attention(q[end], k2, v2, table, P2, 0.25)
+    assert np.abs(o_dec - o_tree[end]).max() <= 1e-12
+    assert np.abs(l_dec - l_tree[end]).max() <= 1e-12

@@ -21,6 +21,7 @@ JT_F32, JT_BF16 = 0, 1
 JT_OK, JT_ERR_INVALID_ARG, JT_ERR_UNSUPPORTED, JT_ERR_WORKSPACE, JT_ERR_LAUNCH = range(5)
 DERR_BAD_LOGIT, DERR_BAD_PARENT, DERR_BAD_NNODES, DERR_BAD_PAGE, DERR_BAD_PREFIX, DERR_BAD_DEPTH = (
     1, 2, 4, 8, 16, 32)
+DERR_BAD_TOKEN, DERR_BAD_PATH = 64, 128
 
 _c_int, _c_size, _vp, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 
@@ -38,6 +39,10 @@ SIGNATURES = {
     "jt_accept_workspace": (_c_size, [_c_int] * 3),
     "jt_accept": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "jt_accept_margin": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
+                                  ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "jt_commit_kv": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
+                              _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -170,3 +175,47 @@ def jt_accept(target_logits, depth_n: int, parent, token, depth, n_nodes, err=No
         _ptr(token), _ptr(depth), _ptr(n_nodes), _ptr(alen), _ptr(anodes), _ptr(bonus),
         _ptr(err), _ptr(ws), ws.numel(), _stream()))
     return alen, anodes, bonus
+
+
+def jt_accept_margin(target_logits, depth_n: int, parent, token, depth, n_nodes,
+                     logit_margin: float, err=None, workspace=None):
+    """Margin acceptance; logit_margin = T ln(theta) (see margin_from_ratio).
+
+    Returns (accept_len [b], accept_nodes [b, depth_n], bonus_token [b]).
+    """
+    lib = load()
+    _cuda(target_logits, "target_logits")
+    b, T, V = target_logits.shape
+    dev = target_logits.device
+    alen = torch.empty((b,), dtype=torch.int32, device=dev)
+    anodes = torch.empty((b, depth_n), dtype=torch.int32, device=dev)
+    bonus = torch.empty((b,), dtype=torch.int32, device=dev)
+    nbytes = lib.jt_accept_workspace(b, T, V)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    _check("jt_accept_margin", lib.jt_accept_margin(
+        _ptr(target_logits), _dtype_code(target_logits), b, T, V, depth_n, _ptr(parent),
+        _ptr(token), _ptr(depth), _ptr(n_nodes), float(logit_margin), _ptr(alen), _ptr(anodes),
+        _ptr(bonus), _ptr(err), _ptr(ws), ws.numel(), _stream()))
+    return alen, anodes, bonus
+
+
+def margin_from_ratio(theta: float, temperature: float = 1.0) -> float:
+    """logit_margin for a probability-ratio threshold theta in (0, 1] at temperature T."""
+    import math
+    return float(temperature) * math.log(float(theta))
+
+
+def jt_commit_kv(k_pool, v_pool, page_table, num_pages, n_nodes, max_nodes: int, accept_len,
+                 accept_nodes, prefix_len, err=None):
+    """Moves the accepted rows next to the prefix in place; advances prefix_len in place."""
+    lib = load()
+    for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool"), (page_table, "page_table"),
+                  (accept_nodes, "accept_nodes"), (prefix_len, "prefix_len")):
+        _cuda(t, nm)
+    hkv, ps, D = k_pool.shape[1], k_pool.shape[2], k_pool.shape[3]
+    b, maxp = page_table.shape
+    depth_n = accept_nodes.shape[1]
+    _check("jt_commit_kv", lib.jt_commit_kv(
+        _ptr(k_pool), _ptr(v_pool), _dtype_code(k_pool), b, hkv, D, _ptr(page_table), maxp,
+        int(num_pages), ps, _ptr(n_nodes), int(max_nodes), depth_n, _ptr(accept_len),
+        _ptr(accept_nodes), _ptr(prefix_len), _ptr(err), _stream()))

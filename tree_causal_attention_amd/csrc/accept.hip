@@ -13,6 +13,9 @@
 // accept_walk: one workgroup per sequence, one thread per node: merges the
 //   chunk winners, marks accepted nodes level by level (parent < child, so a
 //   level only reads the previous one) and picks the deepest accepted node.
+//   The same walk runs the margin rule of jt_accept_margin (AdaptiveSpec page,
+//   kongchang.com, section on the per-step margin rule): a drafted token is
+//   kept when its target probability over the top-1's reaches a threshold.
 #include "jt_device.h"
 #include "jt_host.h"
 
@@ -103,13 +106,21 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax(
   }
 }
 
+// mode 0 (greedy): node v is accepted iff its parent is and token[v] equals the
+//   parent row's argmax.
+// mode 1 (margin): node v is accepted iff its parent is and
+//   (double)L[parent][token[v]] - (double)max L[parent] >= margin (fp64, exact
+//   difference of the stored values); the logit is gathered from `logits`.
+template <typename T>
 __global__ __launch_bounds__(kWalkThreads) void accept_walk(
     const float* __restrict__ part_val, const int* __restrict__ part_idx, int chunks,
     int max_nodes, int depth_n, const int32_t* __restrict__ parent,
     const int32_t* __restrict__ token, const int32_t* __restrict__ depth,
     const int32_t* __restrict__ n_nodes, int32_t* __restrict__ accept_len,
-    int32_t* __restrict__ accept_nodes, int32_t* __restrict__ bonus_token, int32_t* err) {
+    int32_t* __restrict__ accept_nodes, int32_t* __restrict__ bonus_token, int32_t* err,
+    const T* __restrict__ logits, int vocab, int mode, double margin) {
   __shared__ int a[1024];
+  __shared__ float mx[1024];
   __shared__ int par[1024];
   __shared__ int dep[1024];
   __shared__ unsigned char acc[1024];
@@ -137,6 +148,7 @@ __global__ __launch_bounds__(kWalkThreads) void accept_walk(
     for (int c = 1; c < chunks; ++c)
       if (better(part_val[o + c], part_idx[o + c], bv, bi)) { bv = part_val[o + c]; bi = part_idx[o + c]; }
     a[v] = bi;
+    mx[v] = bv;
     par[v] = parent[base + v];
     dep[v] = depth[base + v];
     acc[v] = (v == 0) ? 1 : 0;
@@ -150,6 +162,7 @@ __global__ __launch_bounds__(kWalkThreads) void accept_walk(
       const int p = par[v];
       if (p < 0 || p >= v) b = JT_DERR_BAD_PARENT;
       else if (dep[v] != dep[p] + 1 || dep[v] > depth_n) b = JT_DERR_BAD_DEPTH;
+      else if (mode == 1 && (token[base + v] < 0 || token[base + v] >= vocab)) b = JT_DERR_BAD_TOKEN;
     }
     if (b) atomicOr(&bad, b);
   }
@@ -163,11 +176,20 @@ __global__ __launch_bounds__(kWalkThreads) void accept_walk(
     for (int k = v; k < depth_n; k += kWalkThreads) nodes_out[k] = -1;
     return;
   }
-  for (int lvl = 1; lvl <= depth_n; ++lvl) {
-    if (v < n && dep[v] == lvl) {
-      const int p = par[v];
-      acc[v] = (acc[p] && token[base + v] == a[p]) ? 1 : 0;
+  // this node's own test on its parent's row (one gathered logit in margin mode)
+  bool pass = false;
+  if (v < n && v > 0) {
+    const int p = par[v];
+    const int t = token[base + v];
+    if (mode == 0) {
+      pass = t == a[p];
+    } else {
+      const double lt = static_cast<double>(load_as_f32(logits, (base + p) * vocab + t));
+      pass = lt - static_cast<double>(mx[p]) >= margin;
     }
+  }
+  for (int lvl = 1; lvl <= depth_n; ++lvl) {
+    if (v < n && dep[v] == lvl) acc[v] = (acc[par[v]] && pass) ? 1 : 0;
     __syncthreads();
   }
   if (v < n && acc[v])
@@ -236,7 +258,7 @@ hipError_t accept_launch(const void* logits, jt_dtype dt, int batch, int max_nod
                          int depth_n, const int32_t* parent, const int32_t* token,
                          const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
                          int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
-                         void* workspace, hipStream_t stream) {
+                         void* workspace, hipStream_t stream, int mode, double margin) {
   ArgmaxPlan p = argmax_plan(batch, max_nodes, vocab, dt == JT_F32 ? 4 : 8);
   if (reinterpret_cast<uintptr_t>(logits) % 16 != 0) p.vec = 1;  // rows not 16-byte aligned
   size_t off_idx, bytes;
@@ -252,9 +274,16 @@ hipError_t accept_launch(const void* logits, jt_dtype dt, int batch, int max_nod
   }
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(accept_walk, dim3(batch), dim3(kWalkThreads), 0, stream, pv, pi, p.chunks,
-                     max_nodes, depth_n, parent, token, depth, n_nodes, accept_len, accept_nodes,
-                     bonus_token, err);
+  if (dt == JT_F32)
+    hipLaunchKernelGGL(accept_walk<float>, dim3(batch), dim3(kWalkThreads), 0, stream, pv, pi,
+                       p.chunks, max_nodes, depth_n, parent, token, depth, n_nodes, accept_len,
+                       accept_nodes, bonus_token, err, static_cast<const float*>(logits), vocab,
+                       mode, margin);
+  else
+    hipLaunchKernelGGL(accept_walk<uint16_t>, dim3(batch), dim3(kWalkThreads), 0, stream, pv,
+                       pi, p.chunks, max_nodes, depth_n, parent, token, depth, n_nodes,
+                       accept_len, accept_nodes, bonus_token, err,
+                       static_cast<const uint16_t*>(logits), vocab, mode, margin);
   return hipGetLastError();
 }
 

@@ -128,13 +128,17 @@ size_t jt_accept_workspace(int batch, int max_nodes, int vocab) {
   return jt::accept_workspace_bytes(batch, max_nodes, vocab);
 }
 
-jt_status jt_accept(const void* target_logits, jt_dtype dt, int batch, int max_nodes, int vocab,
-                    int depth_n, const int32_t* parent, const int32_t* token,
-                    const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
-                    int32_t* accept_nodes, int32_t* bonus_token, int32_t* err, void* workspace,
-                    size_t workspace_bytes, void* stream) {
+namespace {
+
+jt_status accept_common(const void* target_logits, jt_dtype dt, int batch, int max_nodes,
+                        int vocab, int depth_n, const int32_t* parent, const int32_t* token,
+                        const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
+                        int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
+                        void* workspace, size_t workspace_bytes, void* stream, int mode,
+                        double margin) {
   if (batch < 0 || max_nodes < 1 || vocab < 1 || depth_n < 1 || !valid_dtype(dt))
     return JT_ERR_INVALID_ARG;
+  if (mode == 1 && !(margin <= 0.0 && std::isfinite(margin))) return JT_ERR_INVALID_ARG;
   if (max_nodes > kMaxNodes || depth_n > kMaxDepth) return JT_ERR_UNSUPPORTED;
   if (batch == 0) return JT_OK;
   if (!target_logits || !parent || !token || !depth || !n_nodes || !accept_len ||
@@ -144,7 +148,53 @@ jt_status jt_accept(const void* target_logits, jt_dtype dt, int batch, int max_n
   if (need > 0 && (!workspace || workspace_bytes < need)) return JT_ERR_WORKSPACE;
   return launched(jt::accept_launch(target_logits, dt, batch, max_nodes, vocab, depth_n, parent,
                                     token, depth, n_nodes, accept_len, accept_nodes, bonus_token,
-                                    err, workspace, static_cast<hipStream_t>(stream)));
+                                    err, workspace, static_cast<hipStream_t>(stream), mode,
+                                    margin));
+}
+
+}  // namespace
+
+jt_status jt_accept(const void* target_logits, jt_dtype dt, int batch, int max_nodes, int vocab,
+                    int depth_n, const int32_t* parent, const int32_t* token,
+                    const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
+                    int32_t* accept_nodes, int32_t* bonus_token, int32_t* err, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  return accept_common(target_logits, dt, batch, max_nodes, vocab, depth_n, parent, token,
+                       depth, n_nodes, accept_len, accept_nodes, bonus_token, err, workspace,
+                       workspace_bytes, stream, 0, 0.0);
+}
+
+jt_status jt_accept_margin(const void* target_logits, jt_dtype dt, int batch, int max_nodes,
+                           int vocab, int depth_n, const int32_t* parent, const int32_t* token,
+                           const int32_t* depth, const int32_t* n_nodes, double logit_margin,
+                           int32_t* accept_len, int32_t* accept_nodes, int32_t* bonus_token,
+                           int32_t* err, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  return accept_common(target_logits, dt, batch, max_nodes, vocab, depth_n, parent, token,
+                       depth, n_nodes, accept_len, accept_nodes, bonus_token, err, workspace,
+                       workspace_bytes, stream, 1, logit_margin);
+}
+
+jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int num_kv_heads,
+                       int head_dim, const int32_t* page_table, int max_pages_per_seq,
+                       int num_pages, int page_size, const int32_t* n_nodes, int max_nodes,
+                       int depth_n, const int32_t* accept_len, const int32_t* accept_nodes,
+                       int32_t* prefix_len, int32_t* err, void* stream) {
+  if (batch < 0 || num_kv_heads < 1 || head_dim < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
+      max_nodes < 1 || depth_n < 1 || !valid_dtype(dt))
+    return JT_ERR_INVALID_ARG;
+  const int row_bytes = head_dim * (dt == JT_F32 ? 4 : 2);
+  if (page_size != 16 || row_bytes % 16 != 0 || depth_n > kMaxDepth || max_nodes > kMaxNodes ||
+      2LL * depth_n * row_bytes > 64 * 1024)
+    return JT_ERR_UNSUPPORTED;
+  if (batch == 0) return JT_OK;
+  if (!k_pool || !v_pool || !page_table || !n_nodes || !accept_len || !accept_nodes ||
+      !prefix_len)
+    return JT_ERR_INVALID_ARG;
+  return launched(jt::commit_kv_launch(k_pool, v_pool, dt == JT_F32 ? 4 : 2, batch, num_kv_heads,
+                                       head_dim, page_table, max_pages_per_seq, num_pages,
+                                       n_nodes, max_nodes, depth_n, accept_len, accept_nodes,
+                                       prefix_len, err, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"
