@@ -502,3 +502,87 @@ def decode_attention(q, k_pool, v_pool, page_table_row, length, scale):
         o[h] = (e @ V[g]) / z
         lse[h] = m + np.log(z)
     return o, lse
+
+
+# ---------------------------------------------------------------------------
+# f2: lossless stochastic verification of the tree (temperature sampling)
+# ---------------------------------------------------------------------------
+
+def softmax_t(row, temperature):
+    """softmax(row / T) in fp64: exp((x - max) / T) / sum (fp64 throughout)."""
+    x = np.asarray(row).astype(np.float64)
+    m = x.max()
+    e = np.exp((x - m) / float(temperature))
+    return e / e.sum()
+
+
+def sample_index(p, u):
+    """Inverse-CDF draw: the smallest index y with cumsum(p)[y] > u * sum(p).
+
+    cumsum in index order (fp64, left to right); u in [0, 1).
+    """
+    c = np.cumsum(np.asarray(p, dtype=np.float64))
+    t = float(u) * c[-1]
+    return int(np.searchsorted(c, t, side="right"))
+
+
+def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes, n_depth,
+                      temperature, u_accept, u_sample):
+    """Stochastic (temperature T > 0) verification of one sequence's tree.
+
+    The SD overview (chooseai.io/news/6515), section on what speculative
+    decoding is, and the AdaptiveSpec page (kongchang.com), section on the
+    strict token-matching rule, state the rule for one drafted token x: with
+    draft distribution q and target distribution p, accept x with probability
+    min(1, p(x) / q(x)); on rejection draw from norm(max(0, p - q)).  The
+    output then has the target's distribution.
+
+    Readings for a tree (the pages state the rule for one token):
+    * p at node u is softmax(target row u / T); q for a child at depth d is
+      softmax(draft row d / T) (candidates are per depth).
+    * At an accepted node, its children are tried in node-index order (= their
+      candidate rank).  Child v (token x) is accepted iff
+      u_accept[v] * q(x) < p(x), with p the current target distribution; on
+      rejection p becomes norm(max(0, p - q)) and the next child is tried.
+    * An accepted child becomes the current node (p = its own target row).
+    * When no child is accepted (or there is none) the walk stops and the
+      bonus token is drawn from the current p with u_sample (sample_index).
+    * If a rejection leaves no mass (max(0, p - q) == 0 everywhere) the
+      remaining children are not tried and the bonus is drawn from p as it
+      was before that rejection.
+    Randomness is passed in: u_accept [n_nodes] (one uniform per node, used
+    when that node is tried), u_sample (one uniform), all in [0, 1).
+    Returns (accept_len, accept_nodes [n_depth], bonus_token).
+    """
+    X = np.asarray(target_logits)
+    Dl = np.asarray(draft_logits)
+    for arr in (np.asarray(X[:n_nodes], dtype=np.float64), np.asarray(Dl, dtype=np.float64)):
+        if np.isnan(arr).any() or np.isposinf(arr).any():
+            raise OracleInputError("logits must not be NaN or +inf")
+        if (arr.max(axis=-1) == -np.inf).any():
+            raise OracleInputError("every logit row needs a finite entry")
+    if not (float(temperature) > 0.0 and np.isfinite(temperature)):
+        raise OracleInputError("temperature must be positive and finite")
+    u = 0
+    path = []
+    while True:
+        p = softmax_t(X[u], temperature)
+        kids = [v for v in range(1, n_nodes) if int(parent[v]) == u]
+        nxt = None
+        for v in kids:
+            q = softmax_t(Dl[int(depth[v]) - 1], temperature)
+            x = int(token[v])
+            if float(u_accept[v]) * q[x] < p[x]:
+                nxt = v
+                break
+            r = np.maximum(p - q, 0.0)
+            if r.sum() == 0.0:
+                break
+            p = r / r.sum()
+        if nxt is None:
+            break
+        path.append(nxt)
+        u = nxt
+    nodes = np.full(n_depth, -1, dtype=np.int64)
+    nodes[:len(path)] = path
+    return len(path), nodes, sample_index(p, u_sample)

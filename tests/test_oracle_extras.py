@@ -148,3 +148,71 @@ def test_commit_then_decode_equals_tree_attention(seed):
     o_dec, l_dec = O.decode_attention(q[end], k2, v2, table, P2, 0.25)
     assert np.abs(o_dec - o_tree[end]).max() <= 1e-12
     assert np.abs(l_dec - l_tree[end]).max() <= 1e-12
+
+
+# ------------------------------------------------------- stochastic verify
+
+def test_stochastic_hand_example():
+    g = json.load(open(os.path.join(GOLDEN, "stochastic_example.json")))
+    X = np.log(np.array(g["target_probs"]))
+    Dl = np.log(np.array(g["draft_probs"]))
+    for c in g["cases"]:
+        ua = np.array([0.0, c["u_accept"]])
+        L, nodes, bonus = O.accept_stochastic(X, Dl, g["parent"], g["token"], g["depth"], 2, 1,
+                                              1.0, ua, c["u_sample"])
+        assert (L, nodes.tolist(), bonus) == (c["accept_len"], c["accept_nodes"], c["bonus"]), c
+
+
+def test_sample_index_is_inverse_cdf():
+    p = np.array([0.0, 0.25, 0.0, 0.5, 0.25])
+    assert [O.sample_index(p, u) for u in (0.0, 0.2, 0.26, 0.74, 0.76, 0.999)] == [1, 1, 3, 3, 4, 4]
+
+
+@pytest.mark.parametrize("k,T", [(1, 1.0), (3, 1.0), (4, 0.7)])
+def test_stochastic_is_lossless_chi_square(k, T):
+    """With k candidates drawn i.i.d. from the draft distribution q, the first
+    token the step emits (the accepted child's, else the bonus) must follow
+    the target distribution p exactly: a chi-square test over many trials."""
+    rng = np.random.default_rng(1000 + 10 * k)
+    V = 6
+    tgt = rng.standard_normal((k + 1, V)) * 1.5
+    dft = rng.standard_normal((1, V)) * 1.5
+    p = O.softmax_t(tgt[0], T)
+    q = O.softmax_t(dft[0], T)
+    trials = 20000
+    counts = np.zeros(V)
+    par = [-1] + [0] * k
+    dep = [0] + [1] * k
+    for _ in range(trials):
+        toks = [0] + [int(t) for t in rng.choice(V, size=k, p=q)]
+        ua = rng.random(k + 1)
+        L, nodes, bonus = O.accept_stochastic(tgt, dft, par, toks, dep, k + 1, 1, T, ua,
+                                              rng.random())
+        counts[toks[nodes[0]] if L else bonus] += 1
+    expected = p * trials
+    chi2 = float(((counts - expected) ** 2 / expected).sum())
+    # 5 degrees of freedom: P(chi2 > 22.1) = 0.0005
+    assert chi2 < 22.1, (chi2, counts, expected)
+
+
+def test_stochastic_deterministic_draft_equal_to_target_accepts():
+    """q == p: every drafted token passes (u * q(x) < p(x) for u < 1)."""
+    rng = np.random.default_rng(5)
+    V, n = 20, 12
+    par, dep = _tree(rng, n)
+    X = rng.standard_normal((n, V))
+    Dl = np.tile(X[0], (max(dep) + 1, 1))
+    # the target row of every node equals the draft row of its children's depth
+    X = np.tile(X[0], (n, 1))
+    tok = [0] + [int(rng.integers(0, V)) for _ in range(1, n)]
+    L, nodes, _ = O.accept_stochastic(X, Dl, par, tok, dep, n, max(dep) + 1, 1.0,
+                                      rng.random(n) * 0.999, 0.5)
+    # the first child of every accepted node is accepted: the path follows first children
+    u, expect = 0, []
+    while True:
+        kids = [v for v in range(1, n) if par[v] == u]
+        if not kids:
+            break
+        u = kids[0]
+        expect.append(u)
+    assert nodes[:L].tolist() == expect
