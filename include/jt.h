@@ -9,6 +9,7 @@
  *   jt_accept          greedy acceptance of the longest matching path
  *   jt_accept_margin   acceptance under a probability-ratio margin
  *   jt_commit_kv       move the accepted path's K/V next to the prefix
+ *   jt_accept_stochastic  lossless verification at temperature T > 0
  *
  * Conventions shared by every call
  * --------------------------------
@@ -65,6 +66,7 @@ typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
 #define JT_DERR_BAD_TOKEN 64  /* a token id outside [0, vocab)                              */
 #define JT_DERR_BAD_PATH 128  /* accept_len outside [0, depth_n], or accept_nodes not a     */
                               /* strictly increasing list of node ids in [1, n_nodes)       */
+#define JT_DERR_BAD_UNIFORM 256 /* a uniform draw outside [0, 1) (or NaN)                   */
 
 /* [host] Static, NUL-terminated description of a status code. */
 const char* jt_status_string(jt_status s);
@@ -282,6 +284,53 @@ jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int n
                        int num_pages, int page_size, const int32_t* n_nodes, int max_nodes,
                        int depth_n, const int32_t* accept_len, const int32_t* accept_nodes,
                        int32_t* prefix_len, int32_t* err, void* stream);
+
+/* ------------------------------------------------------------------------
+ * jt_accept_stochastic -- lossless verification at temperature T > 0.
+ *
+ * Single-token rule (SD overview, chooseai.io/news/6515, section on what
+ * speculative decoding is; AdaptiveSpec page, kongchang.com, section on the
+ * strict token-matching rule): with draft distribution q and target
+ * distribution p, a drafted token x is accepted with probability
+ * min(1, p(x) / q(x)); on rejection the next token is drawn from
+ * norm(max(0, p - q)), which leaves the output distributed as the target's.
+ *
+ * Tree walk fixed here (the pages state the rule for one token):
+ *  - p at node u = softmax(target row u / T); q of a depth-d child =
+ *    softmax(draft row d / T) (the drafter's distributions are per depth).
+ *  - Starting at the root, the current node's children are tried in node-index
+ *    order: child v (token x) is accepted iff u_accept[v] * q(x) < p(x) with p
+ *    the current distribution; a rejection sets p = norm(max(0, p - q)) and
+ *    the next child is tried; if that residual is all zero the remaining
+ *    children are skipped and p stays as it was.  An accepted child becomes
+ *    the current node.
+ *  - When no child is accepted the walk stops; bonus_token is the smallest
+ *    y with sum_{i <= y} p(i) > u_sample * sum_i p(i) (index order).
+ * Arithmetic: fp64 on the stored logit values (exp of the device math
+ * library); different summation orders from a sequential fp64 reference only
+ * move decisions whose margin is at the rounding level (~1e-13 relative).
+ *
+ *   target_logits [batch, max_nodes, vocab]  dt; rows >= n_nodes not read.
+ *   draft_logits  [batch, depth_n, vocab]    dt (row d-1 = depth d).
+ *   parent, token, depth, n_nodes   as jt_accept.
+ *   temperature   > 0 and finite.
+ *   u_accept  [batch, max_nodes] f32: uniform in [0, 1) per node (entry 0 and
+ *             entries >= n_nodes are not read).
+ *   u_sample  [batch] f32: uniform in [0, 1).
+ *   accept_len, accept_nodes, bonus_token  (out) as jt_accept.
+ *   err       JT_DERR_BAD_LOGIT (NaN / +inf, or a row with no finite entry),
+ *             JT_DERR_BAD_NNODES, JT_DERR_BAD_PARENT, JT_DERR_BAD_DEPTH,
+ *             JT_DERR_BAD_TOKEN, JT_DERR_BAD_UNIFORM (that sequence's outputs
+ *             are then zero / -1).
+ * Limits: batch >= 0, 1 <= max_nodes <= 1024, vocab >= 1, 1 <= depth_n <= 64.
+ * One workgroup per sequence; no workspace.
+ * ---------------------------------------------------------------------- */
+jt_status jt_accept_stochastic(const void* target_logits, const void* draft_logits, jt_dtype dt,
+                               int batch, int max_nodes, int vocab, int depth_n,
+                               const int32_t* parent, const int32_t* token, const int32_t* depth,
+                               const int32_t* n_nodes, float temperature, const float* u_accept,
+                               const float* u_sample, int32_t* accept_len, int32_t* accept_nodes,
+                               int32_t* bonus_token, int32_t* err, void* stream);
 
 #ifdef __cplusplus
 }

@@ -527,7 +527,7 @@ def sample_index(p, u):
 
 
 def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes, n_depth,
-                      temperature, u_accept, u_sample):
+                      temperature, u_accept, u_sample, margins=None):
     """Stochastic (temperature T > 0) verification of one sequence's tree.
 
     The SD overview (chooseai.io/news/6515), section on what speculative
@@ -553,6 +553,13 @@ def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes
     Randomness is passed in: u_accept [n_nodes] (one uniform per node, used
     when that node is tried), u_sample (one uniform), all in [0, 1).
     Returns (accept_len, accept_nodes [n_depth], bonus_token).
+
+    margins: optional list; each decision appends how far it was from flipping,
+    relative to the quantities compared (|u q(x) - p(x)| / max(p(x), u q(x))
+    per tried child, and the distance of u_sample * sum from the neighbouring
+    cumulative sums over the total for the bonus).  An implementation that sums
+    in another order may take a different decision only where this is at the
+    rounding level.
     """
     X = np.asarray(target_logits)
     Dl = np.asarray(draft_logits)
@@ -572,7 +579,11 @@ def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes
         for v in kids:
             q = softmax_t(Dl[int(depth[v]) - 1], temperature)
             x = int(token[v])
-            if float(u_accept[v]) * q[x] < p[x]:
+            lhs = float(u_accept[v]) * q[x]
+            if margins is not None:
+                den = max(p[x], lhs)
+                margins.append(abs(lhs - p[x]) / den if den > 0.0 else 1.0)
+            if lhs < p[x]:
                 nxt = v
                 break
             r = np.maximum(p - q, 0.0)
@@ -585,4 +596,10 @@ def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes
         u = nxt
     nodes = np.full(n_depth, -1, dtype=np.int64)
     nodes[:len(path)] = path
-    return len(path), nodes, sample_index(p, u_sample)
+    y = sample_index(p, u_sample)
+    if margins is not None:
+        c = np.cumsum(p)
+        t = float(u_sample) * c[-1]
+        lo = c[y - 1] if y > 0 else 0.0
+        margins.append(min(c[y] - t, t - lo) / c[-1])
+    return len(path), nodes, y

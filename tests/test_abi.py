@@ -151,3 +151,21 @@ def test_commit_kv_validation(lib):
     assert call(hkv=0) == B.JT_ERR_INVALID_ARG
     assert call(dt=3) == B.JT_ERR_INVALID_ARG
     assert call(b=0) == B.JT_OK
+
+
+def test_accept_stochastic_validation(lib):
+    f = lib.jt_accept_stochastic
+    p = ctypes.c_void_p(1)
+
+    def call(temp=0.7, dt=1, b=1, T=17, V=100, N=4, ua=p):
+        return f(p, p, dt, b, T, V, N, p, p, p, p, temp, ua, p, p, p, p, None, None)
+
+    assert call(temp=0.0) == B.JT_ERR_INVALID_ARG
+    assert call(temp=-1.0) == B.JT_ERR_INVALID_ARG
+    assert call(temp=float("inf")) == B.JT_ERR_INVALID_ARG
+    assert call(temp=float("nan")) == B.JT_ERR_INVALID_ARG
+    assert call(dt=2) == B.JT_ERR_INVALID_ARG
+    assert call(N=65) == B.JT_ERR_UNSUPPORTED
+    assert call(T=1025) == B.JT_ERR_UNSUPPORTED
+    assert call(ua=None) == B.JT_ERR_INVALID_ARG
+    assert call(b=0) == B.JT_OK

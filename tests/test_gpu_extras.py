@@ -1,6 +1,8 @@
-"""GPU parity of the margin acceptance (jt_accept_margin) and the KV commit
-(jt_commit_kv) against the CPU oracle: bit-exact integer outputs and bit-exact
-committed pools."""
+"""GPU parity of the margin acceptance (jt_accept_margin), the KV commit
+(jt_commit_kv) and the stochastic verification (jt_accept_stochastic) against
+the CPU oracle: bit-exact integer outputs and committed pools (stochastic
+decisions compared wherever the oracle's walk is not within rounding of a
+flip), plus a chi-square test of the device's output distribution."""
 import json
 import os
 
@@ -275,3 +277,195 @@ def test_commit_then_decode_matches_tree_attention():
         end = int(c["anodes"][s][c["alen"][s] - 1]) if c["alen"][s] > 0 else 0
         check_attention(o_dec[s, 0].double().cpu().numpy(), o_tree[s, end].double().cpu().numpy(),
                         "bf16", f"seq {s}")
+
+
+# ------------------------------------------------------- stochastic verify
+
+_REL_FLIP = 1e-9  # decisions closer than this to flipping may differ by summation order
+
+
+def _gpu_stochastic(X, Dl, parents, tokens, depths, ns, temp, ua, us):
+    d = dev()
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    i32 = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.int32).to(d)
+    f32 = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float32)).to(d)
+    alen, anodes, bonus = B.jt_accept_stochastic(
+        X.to(d).contiguous(), Dl.to(d).contiguous(), i32(parents), i32(tokens), i32(depths),
+        i32(ns), temp, f32(ua), f32(us), err=err)
+    torch.cuda.synchronize()
+    return to_np(alen), to_np(anodes), to_np(bonus), int(err.item())
+
+
+def _compare_stochastic(Xf, Df, pars, toks, deps, ns, N, temp, ua, us, alen, anodes, bonus):
+    """Exact agreement wherever no decision of the oracle's walk is within
+    rounding of flipping; returns the number of sequences compared."""
+    compared = 0
+    for s in range(len(ns)):
+        margins = []
+        L, nodes, bb = O.accept_stochastic(Xf[s], Df[s], pars[s], toks[s], deps[s], ns[s], N,
+                                           temp, np.asarray(ua[s], dtype=np.float32),
+                                           np.float32(us[s]), margins=margins)
+        if min(margins) < _REL_FLIP:
+            continue
+        compared += 1
+        assert (int(alen[s]), int(bonus[s])) == (L, bb), f"seq {s}"
+        assert np.array_equal(anodes[s], nodes), f"seq {s}"
+    return compared
+
+
+def test_stochastic_page_example_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "stochastic_example.json")))
+    X = torch.from_numpy(np.log(np.array(g["target_probs"])).astype(np.float32))[None]
+    Dl = torch.from_numpy(np.log(np.array(g["draft_probs"])).astype(np.float32))[None]
+    for c in g["cases"]:
+        alen, anodes, bonus, err = _gpu_stochastic(X, Dl, [g["parent"]], [g["token"]],
+                                                   [g["depth"]], [2], 1.0,
+                                                   [[0.0, c["u_accept"]]], [c["u_sample"]])
+        assert err == 0
+        assert (int(alen[0]), anodes[0].tolist(), int(bonus[0])) == (
+            c["accept_len"], c["accept_nodes"], c["bonus"]), c
+
+
+def _correlated_case(rng, b, T, V, N, noise):
+    """Random trees whose target rows are the children's draft row plus noise,
+    so acceptances and rejections both happen often."""
+    pars, deps, toks, ns = [], [], [], []
+    Dl = rng.standard_normal((b, N, V)) * 2.0
+    X = rng.standard_normal((b, T, V)) * 2.0
+    for s in range(b):
+        n = int(rng.integers(1, T + 1))
+        while True:
+            p, dd = _tree(rng, n)
+            if max(dd) <= N:
+                break
+        pars.append(p)
+        deps.append(dd)
+        tk = [0]
+        for v in range(1, n):  # draft-likely tokens: sample from the depth's draft row
+            row = Dl[s, dd[v] - 1]
+            w = np.exp(row - row.max())
+            tk.append(int(rng.choice(V, p=w / w.sum())))
+        toks.append(tk)
+        ns.append(n)
+        for u in range(n):
+            if dd[u] < N:
+                X[s, u] = Dl[s, dd[u]] + noise * rng.standard_normal(V)
+    return X, Dl, pars, deps, toks, ns
+
+
+@pytest.mark.parametrize("seed,dtype,temp", [(0, "f32", 1.0), (1, "bf16", 1.0), (2, "f32", 0.5),
+                                             (3, "bf16", 1.75), (4, "f32", 0.25),
+                                             (5, "bf16", 0.5)])
+def test_stochastic_small_random_trees(seed, dtype, temp):
+    rng = np.random.default_rng(700 + seed)
+    b, T, V, N = 16, 60, 40, 12
+    X, Dl, pars, deps, toks, ns = _correlated_case(rng, b, T, V, N, noise=0.6)
+    ua = rng.random((b, T)).astype(np.float32)
+    us = rng.random(b).astype(np.float32)
+    Xt = torch.from_numpy(X.astype(np.float32))
+    Dt = torch.from_numpy(Dl.astype(np.float32))
+    if dtype == "bf16":
+        Xt, Dt = Xt.to(torch.bfloat16), Dt.to(torch.bfloat16)
+    alen, anodes, bonus, err = _gpu_stochastic(Xt, Dt, _pad(pars, T), _pad(toks, T, 0),
+                                               _pad(deps, T), ns, temp, ua, us)
+    assert err == 0
+    n_cmp = _compare_stochastic(Xt.float().numpy(), Dt.float().numpy(), pars, toks, deps, ns, N,
+                                temp, ua, us, alen, anodes, bonus)
+    assert n_cmp >= b - 1
+    assert (alen > 0).any() and (alen < np.array([max(d) for d in deps])).any()
+
+
+def test_stochastic_draft_equal_to_target_follows_first_children():
+    rng = np.random.default_rng(31)
+    V, n, N = 64, 40, 40
+    par, dep = _tree(rng, n)
+    row = rng.standard_normal(V).astype(np.float32)
+    X = torch.from_numpy(np.tile(row, (1, n, 1)))
+    Dl = torch.from_numpy(np.tile(row, (1, N, 1)))
+    tok = [0] + [int(t) for t in rng.integers(0, V, n - 1)]
+    ua = (rng.random((1, n)) * 0.999).astype(np.float32)
+    alen, anodes, bonus, err = _gpu_stochastic(X, Dl, [par], [tok], [dep], [n], 1.0, ua, [0.5])
+    assert err == 0
+    L, nodes, bb = O.accept_stochastic(X[0].numpy(), Dl[0].numpy(), par, tok, dep, n, N, 1.0,
+                                       ua[0], np.float32(0.5))
+    assert (int(alen[0]), anodes[0].tolist(), int(bonus[0])) == (L, nodes.tolist(), bb)
+    u, first_children = 0, []
+    while any(par[v] == u for v in range(n)):
+        u = min(v for v in range(n) if par[v] == u)
+        first_children.append(u)
+    assert anodes[0][:L].tolist() == first_children
+
+
+def test_stochastic_workload_tree(oracle_trees_extras):
+    """The B=256 tree over the 151936-token vocabulary (two sequences); target
+    rows are the children's draft row plus noise."""
+    name = "qwen3_8b_b256"
+    w = WL.WORKLOADS[name]
+    xs = [WL.make_inputs(w, inst, with_target=False) for inst in (0, 1)]
+    trees = [oracle_trees_extras(name, inst, xs[inst], w)[0] for inst in (0, 1)]
+    draft = torch.cat([x.draft for x in xs])
+    rng = np.random.default_rng(11)
+    T, V, N = w.max_nodes, w.vocab, w.depth_n
+    X = torch.empty((2, T, V), dtype=torch.float32)
+    pars, toks, deps, ns = [], [], [], []
+    for s, t in enumerate(trees):
+        n = t["n_nodes"]
+        X[s] = torch.from_numpy(rng.standard_normal((T, V)).astype(np.float32) * 4.0)
+        for u in range(n):
+            du = int(t["depth"][u])
+            if du < N:
+                X[s, u] = draft[s, du] + torch.from_numpy(
+                    rng.standard_normal(V).astype(np.float32) * 0.3)
+        pars.append(t["parent"][:n].tolist())
+        toks.append(t["token"][:n].tolist())
+        deps.append(t["depth"][:n].tolist())
+        ns.append(n)
+    ua = rng.random((2, T)).astype(np.float32)
+    us = rng.random(2).astype(np.float32)
+    for dtype in ("f32", "bf16"):
+        Xt, Dt = (X, draft) if dtype == "f32" else (X.to(torch.bfloat16),
+                                                    draft.to(torch.bfloat16))
+        _say(f"stochastic workload {name} {dtype}")
+        alen, anodes, bonus, err = _gpu_stochastic(Xt, Dt, _pad(pars, T), _pad(toks, T, 0),
+                                                   _pad(deps, T), ns, 1.0, ua, us)
+        assert err == 0
+        n_cmp = _compare_stochastic(Xt.float().numpy(), Dt.float().numpy(), pars, toks, deps, ns,
+                                    N, 1.0, ua, us, alen, anodes, bonus)
+        assert n_cmp == 2
+
+
+@pytest.mark.parametrize("k,temp", [(1, 1.0), (4, 0.7)])
+def test_stochastic_gpu_output_follows_target_chi_square(k, temp):
+    """Losslessness on the device: 8192 sequences, each a root with k children
+    whose tokens are drawn from q; the first emitted token (accepted child's,
+    else the bonus) must follow p = softmax(root row / T)."""
+    rng = np.random.default_rng(90 + k)
+    b, V = 8192, 8
+    root_row = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    drow = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    X = torch.from_numpy(np.tile(root_row, (b, k + 1, 1)))
+    Dl = torch.from_numpy(np.tile(drow, (b, 1, 1)))
+    q = O.softmax_t(drow, temp)
+    toks = np.zeros((b, k + 1), dtype=np.int64)
+    toks[:, 1:] = rng.choice(V, size=(b, k), p=q)
+    par = [[-1] + [0] * k] * b
+    dep = [[0] + [1] * k] * b
+    ua = rng.random((b, k + 1)).astype(np.float32)
+    us = rng.random(b).astype(np.float32)
+    alen, anodes, bonus, err = _gpu_stochastic(X, Dl, par, toks, dep, [k + 1] * b, temp, ua, us)
+    assert err == 0
+    first = np.where(alen > 0, toks[np.arange(b), np.maximum(anodes[:, 0], 0)], bonus)
+    counts = np.bincount(first, minlength=V)
+    expected = O.softmax_t(root_row, temp) * b
+    chi2 = float(((counts - expected) ** 2 / expected).sum())
+    assert chi2 < 26.1, (chi2, counts, expected)  # 7 degrees of freedom, P = 0.0005
+
+
+def test_stochastic_rejects_bad_uniform():
+    X = torch.zeros((2, 2, 8))
+    Dl = torch.zeros((2, 1, 8))
+    alen, anodes, bonus, err = _gpu_stochastic(X, Dl, [[-1, 0]] * 2, [[0, 3]] * 2, [[0, 1]] * 2,
+                                               [2, 2], 1.0, [[0.0, 0.5], [0.0, 0.5]], [0.3, 1.0])
+    assert err & B.DERR_BAD_UNIFORM
+    assert int(alen[1]) == 0 and int(bonus[1]) == -1
+    assert int(bonus[0]) >= 0

@@ -21,7 +21,7 @@ JT_F32, JT_BF16 = 0, 1
 JT_OK, JT_ERR_INVALID_ARG, JT_ERR_UNSUPPORTED, JT_ERR_WORKSPACE, JT_ERR_LAUNCH = range(5)
 DERR_BAD_LOGIT, DERR_BAD_PARENT, DERR_BAD_NNODES, DERR_BAD_PAGE, DERR_BAD_PREFIX, DERR_BAD_DEPTH = (
     1, 2, 4, 8, 16, 32)
-DERR_BAD_TOKEN, DERR_BAD_PATH = 64, 128
+DERR_BAD_TOKEN, DERR_BAD_PATH, DERR_BAD_UNIFORM = 64, 128, 256
 
 _c_int, _c_size, _vp, _c_float = ctypes.c_int, ctypes.c_size_t, ctypes.c_void_p, ctypes.c_float
 
@@ -43,6 +43,8 @@ SIGNATURES = {
                                   ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "jt_commit_kv": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
                               _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
+    "jt_accept_stochastic": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
+                                      _vp, _vp, _c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
 }
 
 
@@ -219,3 +221,34 @@ def jt_commit_kv(k_pool, v_pool, page_table, num_pages, n_nodes, max_nodes: int,
         _ptr(k_pool), _ptr(v_pool), _dtype_code(k_pool), b, hkv, D, _ptr(page_table), maxp,
         int(num_pages), ps, _ptr(n_nodes), int(max_nodes), depth_n, _ptr(accept_len),
         _ptr(accept_nodes), _ptr(prefix_len), _ptr(err), _stream()))
+
+
+def jt_accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes,
+                         temperature: float, u_accept, u_sample, err=None):
+    """Lossless verification at temperature T > 0 with caller-supplied uniforms.
+
+    u_accept [b, max_nodes] f32, u_sample [b] f32, all in [0, 1).
+    Returns (accept_len [b], accept_nodes [b, depth_n], bonus_token [b]).
+    """
+    lib = load()
+    for t, nm in ((target_logits, "target_logits"), (draft_logits, "draft_logits"),
+                  (u_accept, "u_accept"), (u_sample, "u_sample")):
+        _cuda(t, nm)
+    if draft_logits.dtype != target_logits.dtype:
+        raise TypeError("target_logits and draft_logits must share a dtype")
+    if u_accept.dtype != torch.float32 or u_sample.dtype != torch.float32:
+        raise TypeError("u_accept and u_sample must be float32")
+    b, T, V = target_logits.shape
+    depth_n = draft_logits.shape[1]
+    if draft_logits.shape != (b, depth_n, V) or tuple(u_accept.shape) != (b, T) or \
+            tuple(u_sample.shape) != (b,):
+        raise ValueError("inconsistent shapes")
+    dev = target_logits.device
+    alen = torch.empty((b,), dtype=torch.int32, device=dev)
+    anodes = torch.empty((b, depth_n), dtype=torch.int32, device=dev)
+    bonus = torch.empty((b,), dtype=torch.int32, device=dev)
+    _check("jt_accept_stochastic", lib.jt_accept_stochastic(
+        _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), b, T, V, depth_n,
+        _ptr(parent), _ptr(token), _ptr(depth), _ptr(n_nodes), float(temperature), _ptr(u_accept),
+        _ptr(u_sample), _ptr(alen), _ptr(anodes), _ptr(bonus), _ptr(err), _stream()))
+    return alen, anodes, bonus
