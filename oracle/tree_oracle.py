@@ -603,3 +603,146 @@ def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes
         lo = c[y - 1] if y > 0 else 0.0
         margins.append(min(c[y] - t, t - lo) / c[-1])
     return len(path), nodes, y
+
+
+# ---------------------------------------------------------------------------
+# f4: build-mode variants (node-block expansion, entropy / mixed priority)
+# ---------------------------------------------------------------------------
+
+def draft_row_entropy(row) -> float:
+    """Shannon entropy (nats, fp64) of softmax(row): -sum p log p over p > 0.
+
+    The JetSpec explainer (techwalker.com), section 五, names the entropy of
+    each position as an alternative priority.  -inf entries have p = 0.
+    """
+    x = np.asarray(row, dtype=np.float64)
+    if np.isnan(x).any() or np.isposinf(x).any() or not np.isfinite(x).any():
+        raise OracleInputError("draft logits must be finite or -inf, one finite")
+    e = np.exp(x - x.max())
+    p = e / e.sum()
+    nz = p > 0.0
+    return float(-(p[nz] * np.log(p[nz])).sum())
+
+
+def variant_key(score, ent, entropy_weight):
+    """Priority of a node of cumulative score ``score`` at a depth of entropy
+    ``ent``: (1 - a) * score - a * ent for a = entropy_weight in [0, 1]; a = 1
+    is the pure per-position entropy priority (the score term is dropped)."""
+    a = float(entropy_weight)
+    if a == 1.0:
+        return -ent
+    return (1.0 - a) * score - a * ent
+
+
+def build_tree_variant(draft_logits, width: int, budget: int, root_token: int,
+                       expand: str = "candidate", entropy_weight: float = 0.0):
+    """Best-first tree of one sequence under a build-mode variant.
+
+    JetSpec explainer (techwalker.com), section 五: a priority queue of
+    candidate nodes; the best is popped and given up to W children, which join
+    the queue, until B nodes are placed.  The same section reports two other
+    priorities, the per-position entropy and a weighted mix of cumulative
+    probability and entropy.  Readings fixed here:
+
+    * ``expand="candidate"`` (the default reading): the queue holds candidates
+      (parent node, rank); a pop places one node; a placed node shallower than
+      N offers its W children.  Ties: parent index, then rank.
+    * ``expand="node_block"``: the queue holds placed nodes shallower than N
+      (the root first); a pop attaches all of that node's W children (rank
+      order, consecutive node indices), cut short when B nodes are placed.
+      Ties: lower node index.
+    * priority = variant_key(score, H_depth, a): score is the cumulative draft
+      log-probability (as in build_tree); H_d is draft_row_entropy of depth d's
+      row, the entropy of the position the node's token sits at.
+    Candidates are per depth (top-W of row d, logit desc then id asc), as in
+    build_tree.  Returns dict(parent, token, depth, score (-1 / -inf padded to
+    B+1), n_nodes, entropy [N], margin, cross_ties): margin is the smallest
+    positive gap between a pop's winner and the best entry left behind, and
+    cross_ties counts pops whose winner tied with an entry of another depth.
+    """
+    L = np.asarray(draft_logits)
+    n_depth = L.shape[0]
+    a = float(entropy_weight)
+    if not 0.0 <= a <= 1.0:
+        raise OracleInputError("entropy_weight must lie in [0, 1]")
+    if expand not in ("candidate", "node_block"):
+        raise OracleInputError("expand must be 'candidate' or 'node_block'")
+    if budget < 0:
+        raise OracleInputError("budget must be >= 0")
+    lse = np.empty(n_depth)
+    ent = np.empty(n_depth)
+    cand_tok = np.empty((n_depth, width), dtype=np.int64)
+    cand_val = np.empty((n_depth, width))
+    for d in range(n_depth):
+        lse[d], cand_tok[d], cand_val[d] = draft_row_stats(L[d], width)
+        ent[d] = draft_row_entropy(L[d])
+    S = [0.0]
+    for d in range(n_depth):
+        S.append(S[-1] + float(lse[d]))
+
+    parent, token, depth, raw, score = [-1], [int(root_token)], [0], [0.0], [0.0]
+    margin, cross = np.inf, 0
+
+    def place(p, k):
+        dd = depth[p] + 1
+        r = raw[p] + float(cand_val[dd - 1, k])
+        parent.append(p)
+        token.append(int(cand_tok[dd - 1, k]))
+        depth.append(dd)
+        raw.append(r)
+        score.append(r - S[dd])
+
+    def pick(keys, ties, depths):
+        """Index of the best entry: key descending, then the tie key ascending."""
+        nonlocal margin, cross
+        kk = np.asarray(keys)
+        best = kk.max()
+        tied = np.flatnonzero(kk == best)
+        i = int(min(tied, key=lambda t: ties[t]))
+        if len(set(depths[t] for t in tied)) > 1:
+            cross += 1
+        rest = kk[kk < best]
+        if rest.size:
+            margin = min(margin, float(best - rest.max()))
+        return i
+
+    if expand == "candidate":
+        f = []  # entries (parent, rank)
+        if n_depth >= 1:
+            f += [(0, k) for k in range(width)]
+        while len(parent) - 1 < budget and f:
+            keys = []
+            for (p, k) in f:
+                dd = depth[p] + 1
+                sc = (raw[p] + float(cand_val[dd - 1, k])) - S[dd]
+                keys.append(variant_key(sc, float(ent[dd - 1]), a))
+            i = pick(keys, f, [depth[p] + 1 for (p, _) in f])
+            p, k = f.pop(i)
+            place(p, k)
+            if depth[-1] < n_depth:
+                v = len(parent) - 1
+                f += [(v, kk) for kk in range(width)]
+    else:
+        q = [0] if n_depth >= 1 else []  # expandable placed nodes
+        while len(parent) - 1 < budget and q:
+            keys = [0.0 if v == 0 else variant_key(score[v], float(ent[depth[v] - 1]), a)
+                    for v in q]
+            i = pick(keys, q, [depth[v] for v in q])
+            u = q.pop(i)
+            for k in range(width):
+                if len(parent) - 1 >= budget:
+                    break
+                place(u, k)
+                if depth[-1] < n_depth:
+                    q.append(len(parent) - 1)
+
+    n = len(parent)
+    size = budget + 1
+    out = dict(parent=np.full(size, -1, dtype=np.int64), token=np.full(size, -1, dtype=np.int64),
+               depth=np.full(size, -1, dtype=np.int64), score=np.full(size, -np.inf))
+    out["parent"][:n] = parent
+    out["token"][:n] = token
+    out["depth"][:n] = depth
+    out["score"][:n] = score
+    out.update(n_nodes=n, entropy=ent, margin=margin, cross_ties=cross)
+    return out

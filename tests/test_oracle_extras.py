@@ -216,3 +216,149 @@ def test_stochastic_deterministic_draft_equal_to_target_accepts():
         u = kids[0]
         expect.append(u)
     assert nodes[:L].tolist() == expect
+
+
+# ------------------------------------------------------- build-mode variants
+
+def _variant_tree(t):
+    n = t["n_nodes"]
+    return [[int(t["parent"][v]), int(t["token"][v]), int(t["depth"][v])] for v in range(1, n)]
+
+
+def test_variant_hand_examples():
+    g = json.load(open(os.path.join(GOLDEN, "build_variant_example.json")))
+    for c in g["cases"]:
+        L = np.log(np.array(c["rows"]))
+        t = O.build_tree_variant(L, 2, c["budget"], 9, c["expand"], c["weight"])
+        assert _variant_tree(t) == c["tree"], c
+    e = g["entropy"]
+    for row, h in zip(e["rows"], e["nats"]):
+        assert abs(O.draft_row_entropy(np.log(np.array(row))) - h) < 1e-12
+
+
+def test_entropy_closed_forms_and_library():
+    from scipy.stats import entropy as sp_entropy
+    rng = np.random.default_rng(3)
+    V = 50
+    assert abs(O.draft_row_entropy(np.zeros(V)) - np.log(V)) < 1e-12            # uniform
+    one = np.full(V, -np.inf)
+    one[7] = 2.0
+    assert O.draft_row_entropy(one) == 0.0                                         # one finite entry
+    k = np.full(V, -np.inf)
+    k[[1, 5, 9, 30]] = -3.5
+    assert abs(O.draft_row_entropy(k) - np.log(4)) < 1e-12                         # k equal entries
+    for _ in range(20):
+        x = rng.standard_normal(V) * 3
+        p = np.exp(x - x.max())
+        assert abs(O.draft_row_entropy(x) - sp_entropy(p / p.sum())) < 1e-12      # library routine
+    # shift invariance
+    x = rng.standard_normal(V)
+    assert abs(O.draft_row_entropy(x + 100.0) - O.draft_row_entropy(x)) < 1e-12
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_variant_candidate_weight0_equals_build_tree(seed):
+    """The variant at weight 0 in candidate mode is the default build (pinned by
+    brute force elsewhere), ties included (coarse logits)."""
+    rng = np.random.default_rng(40 + seed)
+    for _ in range(30):
+        N, W = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        V = int(rng.integers(W, 12))
+        B = int(rng.integers(0, 30))
+        L = np.round(rng.standard_normal((N, V)) * 2, 1).astype(np.float32)
+        a, b = O.build_tree(L, W, B, 7), O.build_tree_variant(L, W, B, 7)
+        assert a["n_nodes"] == b["n_nodes"]
+        for key in ("parent", "token", "depth", "score"):
+            assert np.array_equal(a[key], b[key])
+
+
+def _complete_tree(L, W):
+    """Every rank path of the complete W-ary tree of depth N: list of
+    (rank path tuple, score list along the path, depth)."""
+    N = L.shape[0]
+    stats = [O.draft_row_stats(L[d], W) for d in range(N)]
+    out = []
+
+    def rec(path, raw, scores):
+        for k in range(W):
+            d = len(path) + 1
+            r = raw + float(stats[d - 1][2][k])
+            s = r - sum(stats[j][0] for j in range(d))
+            p2 = path + (k,)
+            out.append((p2, scores + [s], d))
+            if d < N:
+                rec(p2, r, scores + [s])
+    rec((), 0.0, [])
+    return out
+
+
+def _rank_paths(t, W, L):
+    """Rank path of every placed node (token -> rank in its depth's top-W)."""
+    N = L.shape[0]
+    cand = [list(O.draft_row_stats(L[d], W)[1]) for d in range(N)]
+    paths = {0: ()}
+    for v in range(1, t["n_nodes"]):
+        d = int(t["depth"][v])
+        paths[v] = paths[int(t["parent"][v])] + (cand[d - 1].index(int(t["token"][v])),)
+    return paths
+
+
+@pytest.mark.parametrize("weight", [0.0, 0.3, 0.7, 1.0])
+def test_variant_candidate_bottleneck_property(weight):
+    """Best-first on a tree with any priority places the nodes whose bottleneck
+    (smallest priority on the root-to-node path) is largest: every placed node's
+    bottleneck is >= every unplaced node's.  Brute force over the complete tree
+    (continuous logits, no ties)."""
+    rng = np.random.default_rng(int(weight * 10) + 60)
+    for _ in range(25):
+        N, W = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        V = int(rng.integers(W + 1, 10))
+        L = rng.standard_normal((N, V)) * 2
+        ent = [O.draft_row_entropy(L[d]) for d in range(N)]
+        allp = _complete_tree(L, W)
+        B = int(rng.integers(0, len(allp) + 2))
+        t = O.build_tree_variant(L, W, B, 0, "candidate", weight)
+        placed = set(_rank_paths(t, W, L).values()) - {()}
+        assert len(placed) == min(B, len(allp))
+        bott = {p: min(O.variant_key(s, ent[i], weight) for i, s in enumerate(sc))
+                for p, sc, d in allp}
+        for p in placed:   # prefix-closed
+            assert p[:-1] == () or p[:-1] in placed
+        if placed and len(placed) < len(allp):
+            assert min(bott[p] for p in placed) >= max(bott[p] for p in bott if p not in placed)
+
+
+@pytest.mark.parametrize("weight", [0.0, 0.5, 1.0])
+def test_variant_node_block_structure(weight):
+    """Node-block: the children of every expanded node are consecutive node
+    indices in rank order; the expanded nodes (those with children) other than
+    the root are the best-first choice among expandable nodes (bottleneck
+    property over the complete tree's depth < N nodes); B is filled unless the
+    complete tree is smaller."""
+    rng = np.random.default_rng(int(weight * 10) + 80)
+    for _ in range(25):
+        N, W = int(rng.integers(1, 4)), int(rng.integers(1, 4))
+        V = int(rng.integers(W + 1, 10))
+        L = rng.standard_normal((N, V)) * 2
+        ent = [O.draft_row_entropy(L[d]) for d in range(N)]
+        allp = _complete_tree(L, W)
+        B = int(rng.integers(0, len(allp) + 2))
+        t = O.build_tree_variant(L, W, B, 0, "node_block", weight)
+        n = t["n_nodes"]
+        assert n - 1 == min(B, len(allp))
+        par = [int(x) for x in t["parent"][:n]]
+        paths = _rank_paths(t, W, L)
+        kids = {}
+        for v in range(1, n):
+            kids.setdefault(par[v], []).append(v)
+        for u, ks in kids.items():
+            assert ks == list(range(ks[0], ks[0] + len(ks)))          # consecutive
+            assert [paths[v][-1] for v in ks] == list(range(len(ks)))  # rank order
+            if ks[-1] != n - 1:                                       # only the last block is cut
+                assert len(ks) == W
+        expanded = {paths[u] for u in kids if u != 0}
+        bott = {p: min(O.variant_key(s, ent[i], weight) for i, s in enumerate(sc))
+                for p, sc, d in allp if d < N}
+        if expanded and len(expanded) < len(bott):
+            assert min(bott[p] for p in expanded) >= max(bott[p] for p in bott
+                                                         if p not in expanded)
