@@ -10,6 +10,8 @@
  *   jt_accept_margin   acceptance under a probability-ratio margin
  *   jt_commit_kv       move the accepted path's K/V next to the prefix
  *   jt_accept_stochastic  lossless verification at temperature T > 0
+ *   jt_build_tree_variant  tree build under the alternative expansions and
+ *                      priorities (node-block, entropy / mixed)
  *
  * Conventions shared by every call
  * --------------------------------
@@ -55,6 +57,9 @@ typedef enum {
 } jt_status;
 
 typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
+
+/* Tree expansion of jt_build_tree_variant. */
+typedef enum { JT_EXPAND_CANDIDATE = 0, JT_EXPAND_NODE_BLOCK = 1 } jt_expand;
 
 /* Device error bits (OR-ed into *err). */
 #define JT_DERR_BAD_LOGIT 1   /* NaN or +inf logit, or a draft row without a finite entry */
@@ -123,6 +128,46 @@ jt_status jt_build_tree(const void* draft_logits, jt_dtype dt, int batch, int de
                         int32_t* parent, int32_t* token, int32_t* depth, double* score,
                         int32_t* n_nodes, int32_t* err, void* workspace,
                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * jt_build_tree_variant -- the tree build under the alternative expansion and
+ * priority rules.
+ *
+ * JetSpec explainer (techwalker.com), section 五: a priority queue whose best
+ * entry is popped and given up to W children until B nodes are placed; the
+ * same section compares the cumulative log-probability priority with the
+ * per-position entropy and with weighted mixes of the two.
+ *
+ * Priority, with a = entropy_weight in [0, 1]:
+ *   key = (1 - a) * score - a * H_d     (a == 1: key = -H_d)
+ * where score is the cumulative draft log-probability (as jt_build_tree) and
+ * H_d = -sum p log p of softmax(draft row d) (fp64, nats) for the depth d of
+ * the node being ranked (lower entropy ranks higher).  The key is evaluated
+ * in fp64 without fused multiply-adds.
+ * expand_mode:
+ *   JT_EXPAND_CANDIDATE   the queue holds candidates (placed node, rank); a
+ *                         pop places one node; ties go to the lower parent
+ *                         index, then the lower rank.  With a = 0 the result
+ *                         equals jt_build_tree.
+ *   JT_EXPAND_NODE_BLOCK  the queue holds placed nodes shallower than N (the
+ *                         root first); a pop attaches all W children of that
+ *                         node (rank order, consecutive node indices), cut
+ *                         short at B; ties go to the lower node index.
+ * Candidates, node numbering (parent[j] < j), outputs, err bits, workspace
+ * (jt_build_tree_workspace) and limits are those of jt_build_tree, except that
+ * no LDS limit applies.  The per-depth lse and entropy are fp64 reductions in
+ * another order than a sequential one: priorities that differ by ~1e-13 may
+ * be ordered differently from a sequential fp64 implementation.
+ * One workgroup per sequence runs the B pops one after another (a workgroup
+ * argmax each); jt_build_tree remains the fast path for the default rule.
+ *   entropy_weight  in [0, 1] (JT_ERR_INVALID_ARG otherwise, NaN included).
+ * ---------------------------------------------------------------------- */
+jt_status jt_build_tree_variant(const void* draft_logits, jt_dtype dt, int batch, int depth_n,
+                                int vocab, int width_w, int budget_b, jt_expand expand_mode,
+                                double entropy_weight, const int32_t* root_token,
+                                int32_t* parent, int32_t* token, int32_t* depth, double* score,
+                                int32_t* n_nodes, int32_t* err, void* workspace,
+                                size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * jt_tree_meta -- ancestor-or-self bitmasks of every node.

@@ -169,3 +169,22 @@ def test_accept_stochastic_validation(lib):
     assert call(T=1025) == B.JT_ERR_UNSUPPORTED
     assert call(ua=None) == B.JT_ERR_INVALID_ARG
     assert call(b=0) == B.JT_OK
+
+
+def test_build_tree_variant_validation(lib):
+    f = lib.jt_build_tree_variant
+    p = ctypes.c_void_p(1)
+    need = lib.jt_build_tree_workspace(1, 4, 100, 4, 16)
+
+    def call(mode=0, a=0.5, dt=0, b=1, N=4, V=100, W=4, Bn=16, ws=need):
+        return f(p, dt, b, N, V, W, Bn, mode, a, p, p, p, p, None, p, None, p, ws, None)
+
+    assert call(mode=2) == B.JT_ERR_INVALID_ARG
+    assert call(a=1.5) == B.JT_ERR_INVALID_ARG
+    assert call(a=-0.1) == B.JT_ERR_INVALID_ARG
+    assert call(a=float("nan")) == B.JT_ERR_INVALID_ARG
+    assert call(W=101) == B.JT_ERR_INVALID_ARG
+    assert call(N=65) == B.JT_ERR_UNSUPPORTED
+    assert call(Bn=1024) == B.JT_ERR_UNSUPPORTED
+    assert call(ws=0) == B.JT_ERR_WORKSPACE
+    assert call(b=0) == B.JT_OK

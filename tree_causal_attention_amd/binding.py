@@ -18,6 +18,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libjt.so")
 
 JT_F32, JT_BF16 = 0, 1
+JT_EXPAND_CANDIDATE, JT_EXPAND_NODE_BLOCK = 0, 1
 JT_OK, JT_ERR_INVALID_ARG, JT_ERR_UNSUPPORTED, JT_ERR_WORKSPACE, JT_ERR_LAUNCH = range(5)
 DERR_BAD_LOGIT, DERR_BAD_PARENT, DERR_BAD_NNODES, DERR_BAD_PAGE, DERR_BAD_PREFIX, DERR_BAD_DEPTH = (
     1, 2, 4, 8, 16, 32)
@@ -31,6 +32,9 @@ SIGNATURES = {
     "jt_build_tree_workspace": (_c_size, [_c_int] * 5),
     "jt_build_tree": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
                                _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "jt_build_tree_variant": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
+                                       ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                       _c_size, _vp]),
     "jt_tree_meta": (_c_int, [_vp, _vp, _c_int, _c_int, _vp, _vp, _vp]),
     "jt_tree_attention_workspace": (_c_size, [_c_int] * 8),
     "jt_tree_attention": (_c_int, [_vp, _vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _c_int,
@@ -120,6 +124,32 @@ def jt_build_tree(draft_logits: torch.Tensor, width_w: int, budget_b: int,
         _ptr(draft_logits), _dtype_code(draft_logits), b, N, V, width_w, budget_b, _ptr(root_token),
         _ptr(out["parent"]), _ptr(out["token"]), _ptr(out["depth"]), _ptr(out["score"]),
         _ptr(out["n_nodes"]), _ptr(err), _ptr(ws), ws.numel(), _stream()))
+    return out
+
+
+def jt_build_tree_variant(draft_logits: torch.Tensor, width_w: int, budget_b: int,
+                          root_token: torch.Tensor, expand: str = "candidate",
+                          entropy_weight: float = 0.0, err: torch.Tensor | None = None,
+                          with_score: bool = True, workspace: torch.Tensor | None = None):
+    """Build-mode variants; expand is "candidate" or "node_block".  Same outputs as jt_build_tree."""
+    lib = load()
+    _cuda(draft_logits, "draft_logits")
+    modes = {"candidate": JT_EXPAND_CANDIDATE, "node_block": JT_EXPAND_NODE_BLOCK}
+    if expand not in modes:
+        raise ValueError(f"unknown expand mode {expand!r}")
+    b, N, V = draft_logits.shape
+    dev = draft_logits.device
+    T = budget_b + 1
+    out = {k: torch.empty((b, T), dtype=torch.int32, device=dev) for k in ("parent", "token", "depth")}
+    out["score"] = torch.empty((b, T), dtype=torch.float64, device=dev) if with_score else None
+    out["n_nodes"] = torch.empty((b,), dtype=torch.int32, device=dev)
+    nbytes = lib.jt_build_tree_workspace(b, N, V, width_w, budget_b)
+    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    _check("jt_build_tree_variant", lib.jt_build_tree_variant(
+        _ptr(draft_logits), _dtype_code(draft_logits), b, N, V, width_w, budget_b, modes[expand],
+        float(entropy_weight), _ptr(root_token), _ptr(out["parent"]), _ptr(out["token"]),
+        _ptr(out["depth"]), _ptr(out["score"]), _ptr(out["n_nodes"]), _ptr(err), _ptr(ws),
+        ws.numel(), _stream()))
     return out
 
 

@@ -64,6 +64,32 @@ jt_status jt_build_tree(const void* draft_logits, jt_dtype dt, int batch, int de
                                         static_cast<hipStream_t>(stream)));
 }
 
+jt_status jt_build_tree_variant(const void* draft_logits, jt_dtype dt, int batch, int depth_n,
+                                int vocab, int width_w, int budget_b, jt_expand expand_mode,
+                                double entropy_weight, const int32_t* root_token,
+                                int32_t* parent, int32_t* token, int32_t* depth, double* score,
+                                int32_t* n_nodes, int32_t* err, void* workspace,
+                                size_t workspace_bytes, void* stream) {
+  if (batch < 0 || depth_n < 1 || vocab < 1 || width_w < 1 || budget_b < 0 || !valid_dtype(dt))
+    return JT_ERR_INVALID_ARG;
+  if (width_w > vocab) return JT_ERR_INVALID_ARG;
+  if (expand_mode != JT_EXPAND_CANDIDATE && expand_mode != JT_EXPAND_NODE_BLOCK)
+    return JT_ERR_INVALID_ARG;
+  if (!(entropy_weight >= 0.0 && entropy_weight <= 1.0)) return JT_ERR_INVALID_ARG;
+  if (depth_n > kMaxDepth || width_w > kMaxWidth || budget_b + 1 > kMaxNodes ||
+      vocab > jt::build_tree_max_vocab())
+    return JT_ERR_UNSUPPORTED;
+  if (batch == 0) return JT_OK;
+  if (!draft_logits || !root_token || !parent || !token || !depth || !n_nodes)
+    return JT_ERR_INVALID_ARG;
+  const size_t need = jt::build_tree_workspace_bytes(batch, depth_n, vocab, width_w);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return JT_ERR_WORKSPACE;
+  return launched(jt::build_tree_variant_launch(
+      draft_logits, dt, batch, depth_n, vocab, width_w, budget_b, static_cast<int>(expand_mode),
+      entropy_weight, root_token, parent, token, depth, score, n_nodes, err, workspace,
+      static_cast<hipStream_t>(stream)));
+}
+
 jt_status jt_tree_meta(const int32_t* parent, const int32_t* n_nodes, int batch, int max_nodes,
                        uint32_t* anc_mask, int32_t* err, void* stream) {
   if (batch < 0 || max_nodes < 1) return JT_ERR_INVALID_ARG;

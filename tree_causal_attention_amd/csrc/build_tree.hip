@@ -57,14 +57,17 @@ constexpr int kCandCap = 1024;  // threshold candidates kept per chunk
 //    only logits >= L are collected in LDS and ranked; if more than kCandCap
 //    qualify (e.g. massive ties) every thread builds its exact sorted top-W and
 //    W rounds of "best head" merge them.
-template <typename T, int WMAX, int VEC, int EPT>
+// ENT: also the fp64 sum of exp(x - max) * (x - max) (the chunk's entropy
+// partial; tree_select_seq merges it into the per-depth entropy).
+template <typename T, int WMAX, int VEC, int EPT, bool ENT>
 __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
     const T* __restrict__ logits, int vocab, int chunks, int chunk_len, int width,
-    float* __restrict__ part_max, double* __restrict__ part_sum, float* __restrict__ part_val,
-    int* __restrict__ part_idx, int32_t* err) {
+    float* __restrict__ part_max, double* __restrict__ part_sum, double* __restrict__ part_ent,
+    float* __restrict__ part_val, int* __restrict__ part_idx, int32_t* err) {
   constexpr int NV = EPT / VEC;
   __shared__ float sm_m[kScanThreads / kWave];
   __shared__ double sm_s[kScanThreads / kWave];
+  __shared__ double sm_t[kScanThreads / kWave];
   __shared__ float sm_tmax[kScanThreads];
   __shared__ float sm_cv[kCandCap];
   __shared__ int sm_ci[kCandCap];
@@ -113,17 +116,24 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   for (int w = 1; w < kScanThreads / kWave; ++w) M = fmaxf(M, sm_m[w]);
 
   // ---- fp64 sum of exp(x - M) over the registers
-  double sacc = 0.0;
+  double sacc = 0.0, tacc = 0.0;
   if (M != -INFINITY) {
     const double Md = static_cast<double>(M);
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-      const double e = exp(static_cast<double>(fmaxf(xv[k], -1.0e30f)) - Md);
-      sacc += (xv[k] != -INFINITY) ? e : 0.0;
+      const double dx = static_cast<double>(fmaxf(xv[k], -1.0e30f)) - Md;
+      const double e = exp(dx);
+      const bool fin = xv[k] != -INFINITY;
+      sacc += fin ? e : 0.0;
+      if constexpr (ENT) tacc += fin ? e * dx : 0.0;
     }
   }
   for (int o = 32; o > 0; o >>= 1) sacc += shfl_xor_f64(sacc, o);
   if (lane == 0) sm_s[wv] = sacc;
+  if constexpr (ENT) {
+    for (int o = 32; o > 0; o >>= 1) tacc += shfl_xor_f64(tacc, o);
+    if (lane == 0) sm_t[wv] = tacc;
+  }
 
   // ---- threshold: the W-th largest thread maximum (ties by thread id)
   int rank = 0;
@@ -138,6 +148,11 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
     for (int w = 0; w < kScanThreads / kWave; ++w) S += sm_s[w];
     part_max[row * chunks + c] = M;
     part_sum[row * chunks + c] = S;
+    if constexpr (ENT) {
+      double Tt = 0.0;
+      for (int w = 0; w < kScanThreads / kWave; ++w) Tt += sm_t[w];
+      part_ent[row * chunks + c] = Tt;
+    }
   }
   const float L = sm_L;
 #pragma unroll
@@ -319,6 +334,76 @@ __device__ __forceinline__ int co_rank(int o, int la, int lb, Prec prec_ab) {
   return lo;
 }
 
+// Merge the chunk partials of every depth of sequence seq (one wave a depth;
+// each lane holds one chunk's sorted candidates in registers): lse[d], the
+// top-W (cval, ctok [d * WMAX + r]) and, when part_ent is given, the entropy
+// ent[d] = log S - T / S with S = sum exp(x - max), T = sum exp(x - max)(x - max).
+template <int WMAX>
+__device__ void merge_depth_partials(const float* __restrict__ part_max,
+                                     const double* __restrict__ part_sum,
+                                     const double* __restrict__ part_ent,
+                                     const float* __restrict__ part_val,
+                                     const int* __restrict__ part_idx, int chunks, int depth_n,
+                                     int width, int seq, double* lse, double* ent, float* cval,
+                                     int* ctok, int32_t* err, int nwaves) {
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  for (int d = wv; d < depth_n; d += nwaves) {
+    const size_t row = static_cast<size_t>(seq) * depth_n + d;
+    const bool act = lane < chunks;
+    const float mc = act ? part_max[row * chunks + lane] : -INFINITY;
+    const double sc = act ? part_sum[row * chunks + lane] : 0.0;
+    float hv[WMAX];
+    int hid[WMAX];
+#pragma unroll
+    for (int k = 0; k < WMAX; ++k) {
+      const bool ok = act && k < width;
+      hv[k] = ok ? part_val[(row * chunks + lane) * width + k] : -INFINITY;
+      hid[k] = ok ? part_idx[(row * chunks + lane) * width + k] : INT32_MAX;
+    }
+    float M = mc;
+    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
+    const double scale =
+        (mc == -INFINITY) ? 0.0 : exp(static_cast<double>(mc) - static_cast<double>(M));
+    double contrib = sc * scale;
+    for (int o = 32; o > 0; o >>= 1) contrib += shfl_xor_f64(contrib, o);
+    double tsum = 0.0;
+    if (part_ent) {
+      // the chunk's terms were taken about its own max mc: shift them to M
+      const double tc = act ? part_ent[row * chunks + lane] : 0.0;
+      tsum = (mc == -INFINITY)
+                 ? 0.0
+                 : scale * (tc + (static_cast<double>(mc) - static_cast<double>(M)) * sc);
+      for (int o = 32; o > 0; o >>= 1) tsum += shfl_xor_f64(tsum, o);
+    }
+    if (lane == 0) {
+      if (M == -INFINITY) {
+        report(err, JT_DERR_BAD_LOGIT);
+        lse[d] = 0.0;
+        if (ent) ent[d] = 0.0;
+      } else {
+        lse[d] = static_cast<double>(M) + log(contrib);
+        if (ent) ent[d] = log(contrib) - tsum / contrib;
+      }
+    }
+    for (int r = 0; r < width; ++r) {
+      float bv = hv[0];
+      int bi = hid[0];
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = shfl_xor(bv, o);
+        const int oi = shfl_xor(bi, o);
+        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+      }
+      if (hid[0] == bi && bi != INT32_MAX) {  // this lane's head won: pop it
+#pragma unroll
+        for (int k = 0; k + 1 < WMAX; ++k) { hv[k] = hv[k + 1]; hid[k] = hid[k + 1]; }
+        hv[WMAX - 1] = -INFINITY;
+        hid[WMAX - 1] = INT32_MAX;
+      }
+      if (lane == 0) { cval[d * WMAX + r] = bv; ctok[d * WMAX + r] = bi; }
+    }
+  }
+}
+
 // One workgroup per sequence.
 //  phase 1: per depth, merge the chunk partials (lse, top-W).
 //  phase 2: per level d, the W candidate columns (children of the sorted level
@@ -358,50 +443,9 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   const int tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
   const int nwaves = kSelectThreads / kWave;
 
-  // ---- phase 1: merge the chunk partials of every depth (one wave a depth);
-  // each lane holds one chunk's sorted candidates in registers.
-  for (int d = wv; d < depth_n; d += nwaves) {
-    const size_t row = static_cast<size_t>(seq) * depth_n + d;
-    const bool act = lane < chunks;
-    const float mc = act ? part_max[row * chunks + lane] : -INFINITY;
-    const double sc = act ? part_sum[row * chunks + lane] : 0.0;
-    float hv[WMAX];
-    int hid[WMAX];
-#pragma unroll
-    for (int k = 0; k < WMAX; ++k) {
-      const bool ok = act && k < width;
-      hv[k] = ok ? part_val[(row * chunks + lane) * width + k] : -INFINITY;
-      hid[k] = ok ? part_idx[(row * chunks + lane) * width + k] : INT32_MAX;
-    }
-    float M = mc;
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
-    double contrib = (mc == -INFINITY) ? 0.0 : sc * exp(static_cast<double>(mc) - static_cast<double>(M));
-    for (int o = 32; o > 0; o >>= 1) contrib += shfl_xor_f64(contrib, o);
-    if (lane == 0) {
-      if (M == -INFINITY) {
-        report(err, JT_DERR_BAD_LOGIT);
-        lse[d] = 0.0;
-      } else {
-        lse[d] = static_cast<double>(M) + log(contrib);
-      }
-    }
-    for (int r = 0; r < width; ++r) {
-      float bv = hv[0];
-      int bi = hid[0];
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = shfl_xor(bv, o);
-        const int oi = shfl_xor(bi, o);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
-      if (hid[0] == bi && bi != INT32_MAX) {  // this lane's head won: pop it
-#pragma unroll
-        for (int k = 0; k + 1 < WMAX; ++k) { hv[k] = hv[k + 1]; hid[k] = hid[k + 1]; }
-        hv[WMAX - 1] = -INFINITY;
-        hid[WMAX - 1] = INT32_MAX;
-      }
-      if (lane == 0) { cval[d * WMAX + r] = bv; ctok[d * WMAX + r] = bi; }
-    }
-  }
+  // ---- phase 1: merge the chunk partials of every depth
+  merge_depth_partials<WMAX>(part_max, part_sum, nullptr, part_val, part_idx, chunks, depth_n,
+                             width, seq, lse, nullptr, cval, ctok, err, nwaves);
   __syncthreads();
   if (tid == 0) {
     S[0] = 0.0;
@@ -550,6 +594,169 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   }
 }
 
+// ------------------------------------------------------------------
+// tree_select_seq: the build-mode variants, as a literal best-first search.
+// JetSpec explainer (techwalker.com), section 五: pop the best entry of a
+// priority queue, give it up to W children, repeat until B nodes are placed;
+// the same section names the per-position entropy and an entropy / log-prob
+// mix as alternative priorities.  With a = entropy_weight in [0, 1]:
+//   key = (1 - a) * score - a * H_depth   (a == 1: key = -H_depth),
+// score the cumulative draft log-probability, H_d the entropy of depth d's
+// row.  expand_mode 0 (candidate): the queue holds candidates (placed node,
+// rank); a pop places one node; ties by parent index, then rank.  The
+// candidates of one parent are key-sorted by rank (top-W is logit-sorted), so
+// each placed node keeps one head: its next unplaced rank.  expand_mode 1
+// (node block): the queue holds placed nodes shallower than N; a pop attaches
+// that node's W children (rank order, consecutive indices), cut at B; ties by
+// node index.
+// One workgroup of 256 threads per sequence; node v lives in thread v % 256,
+// slot v / 256 (4 slots cover the 1024-node maximum).  Each pop is one
+// workgroup argmax (wave shuffles, one barrier).
+constexpr int kSeqThreads = 256;
+constexpr int kSeqSlots = 1024 / kSeqThreads;
+constexpr int kSeqWaves = kSeqThreads / kWave;
+
+__device__ __forceinline__ double variant_key(double score, double ent, double a) {
+#pragma clang fp contract(off)
+  if (a == 1.0) return -ent;
+  return (1.0 - a) * score - a * ent;
+}
+
+// (key, id) order: larger key first, then smaller id; id < 0 = empty.
+__device__ __forceinline__ bool seq_better(double ka, int ia, double kb, int ib) {
+  if (ia < 0) return false;
+  if (ib < 0) return true;
+  return ka > kb || (ka == kb && ia < ib);
+}
+
+template <int WMAX>
+__global__ __launch_bounds__(kSeqThreads) void tree_select_seq(
+    const float* __restrict__ part_max, const double* __restrict__ part_sum,
+    const double* __restrict__ part_ent, const float* __restrict__ part_val,
+    const int* __restrict__ part_idx, int chunks, int depth_n, int width, int budget,
+    int expand_mode, double a, const int32_t* __restrict__ root_token,
+    int32_t* __restrict__ parent, int32_t* __restrict__ token, int32_t* __restrict__ depth,
+    double* __restrict__ score_out, int32_t* __restrict__ n_nodes, int32_t* err) {
+  __shared__ double lse[64], ent[64], S[65];
+  __shared__ float cval[64 * WMAX];
+  __shared__ int ctok[64 * WMAX];
+  __shared__ double raw[1024];
+  __shared__ int dep[1024];
+  __shared__ double red_k[2][kSeqWaves];
+  __shared__ int red_i[2][kSeqWaves];
+  const int seq = blockIdx.x, tid = threadIdx.x, lane = tid % kWave, wv = tid / kWave;
+
+  merge_depth_partials<WMAX>(part_max, part_sum, part_ent, part_val, part_idx, chunks, depth_n,
+                             width, seq, lse, ent, cval, ctok, err, kSeqWaves);
+  __syncthreads();
+  if (tid == 0) {
+    S[0] = 0.0;
+    for (int d = 0; d < depth_n; ++d) S[d + 1] = S[d] + lse[d];
+    raw[0] = 0.0;
+    dep[0] = 0;
+  }
+  __syncthreads();
+
+  const size_t base = static_cast<size_t>(seq) * (budget + 1);
+  // per-slot queue entry: key and id (candidate: node << 5 | rank; block: node)
+  double qk[kSeqSlots];
+  int qi[kSeqSlots];
+#pragma unroll
+  for (int s = 0; s < kSeqSlots; ++s) { qk[s] = 0.0; qi[s] = -1; }
+  // key of the candidate (u, k), u placed at depth du < depth_n
+  auto cand_key = [&](int u, int du, int k) {
+    const double sc = (raw[u] + static_cast<double>(cval[du * WMAX + k])) - S[du + 1];
+    return variant_key(sc, ent[du], a);
+  };
+  if (tid == 0 && depth_n >= 1) {  // node 0 = thread 0, slot 0
+    qi[0] = 0;
+    qk[0] = expand_mode == 0 ? cand_key(0, 0, 0) : 0.0;
+  }
+
+  int n = 1;  // placed nodes (uniform)
+  for (int pop = 0; n - 1 < budget; ++pop) {
+    // ---- argmax over the queue
+    double bk = 0.0;
+    int bi = -1;
+#pragma unroll
+    for (int s = 0; s < kSeqSlots; ++s)
+      if (seq_better(qk[s], qi[s], bk, bi)) { bk = qk[s]; bi = qi[s]; }
+    for (int o = 32; o > 0; o >>= 1) {
+      const double ok = __shfl_xor(bk, o, kWave);
+      const int oi = __shfl_xor(bi, o, kWave);
+      if (seq_better(ok, oi, bk, bi)) { bk = ok; bi = oi; }
+    }
+    const int par = pop & 1;
+    if (lane == 0) { red_k[par][wv] = bk; red_i[par][wv] = bi; }
+    __syncthreads();
+    bk = red_k[par][0];
+    bi = red_i[par][0];
+    for (int w = 1; w < kSeqWaves; ++w)
+      if (seq_better(red_k[par][w], red_i[par][w], bk, bi)) { bk = red_k[par][w]; bi = red_i[par][w]; }
+    if (bi < 0) break;  // queue empty (uniform)
+    if (expand_mode == 0) {
+      const int u = bi >> 5, k = bi & 31;
+      const int du = dep[u];
+      const int v = n;
+      const double rv = raw[u] + static_cast<double>(cval[du * WMAX + k]);
+      if (tid == u % kSeqThreads) {  // advance u's head
+        const int s = u / kSeqThreads;
+        if (k + 1 < width) { qi[s] = (u << 5) | (k + 1); qk[s] = cand_key(u, du, k + 1); }
+        else qi[s] = -1;
+      }
+      if (tid == v % kSeqThreads) {  // place v, open its head
+        const int s = v / kSeqThreads;
+        raw[v] = rv;
+        dep[v] = du + 1;
+        parent[base + v] = u;
+        token[base + v] = ctok[du * WMAX + k];
+        depth[base + v] = du + 1;
+        if (score_out) score_out[base + v] = rv - S[du + 1];
+        if (du + 1 < depth_n) {
+          qi[s] = v << 5;
+          const double sc = (rv + static_cast<double>(cval[(du + 1) * WMAX])) - S[du + 2];
+          qk[s] = variant_key(sc, ent[du + 1], a);
+        }
+      }
+      n += 1;
+    } else {
+      const int u = bi;
+      const int du = dep[u];
+      const int c = min(width, budget - (n - 1));
+      if (tid == u % kSeqThreads) qi[u / kSeqThreads] = -1;
+      for (int k = 0; k < c; ++k) {
+        const int v = n + k;
+        if (tid == v % kSeqThreads) {
+          const int s = v / kSeqThreads;
+          const double rv = raw[u] + static_cast<double>(cval[du * WMAX + k]);
+          const double sc = rv - S[du + 1];
+          raw[v] = rv;
+          dep[v] = du + 1;
+          parent[base + v] = u;
+          token[base + v] = ctok[du * WMAX + k];
+          depth[base + v] = du + 1;
+          if (score_out) score_out[base + v] = sc;
+          if (du + 1 < depth_n) { qi[s] = v; qk[s] = variant_key(sc, ent[du], a); }
+        }
+      }
+      n += c;
+    }
+  }
+  for (int g = n + tid; g <= budget; g += kSeqThreads) {
+    parent[base + g] = -1;
+    token[base + g] = -1;
+    depth[base + g] = -1;
+    if (score_out) score_out[base + g] = -INFINITY;
+  }
+  if (tid == 0) {
+    parent[base] = -1;
+    token[base] = root_token[seq];
+    depth[base] = 0;
+    if (score_out) score_out[base] = 0.0;
+    n_nodes[seq] = n;
+  }
+}
+
 // ------------------------------------------------------------------ host side
 
 struct ScanPlan {
@@ -574,7 +781,7 @@ static ScanPlan scan_plan(int batch, int depth_n, int vocab, int width, int vec)
 }
 
 struct ScanWorkspace {
-  size_t off_max, off_sum, off_val, off_idx, bytes;
+  size_t off_max, off_sum, off_ent, off_val, off_idx, bytes;
 };
 
 static ScanWorkspace scan_workspace(const ScanPlan& p, int width) {
@@ -584,6 +791,7 @@ static ScanWorkspace scan_workspace(const ScanPlan& p, int width) {
   auto take = [&](size_t b) { o = (o + 255) / 256 * 256; size_t r = o; o += b; return r; };
   w.off_max = take(n * sizeof(float));
   w.off_sum = take(n * sizeof(double));
+  w.off_ent = take(n * sizeof(double));
   w.off_val = take(n * width * sizeof(float));
   w.off_idx = take(n * width * sizeof(int));
   w.bytes = (o + 255) / 256 * 256;
@@ -602,80 +810,135 @@ size_t build_tree_lds_bytes(int depth_n, int width, int budget) {
   return select_layout(depth_n, width, budget, wmax_of(width)).bytes;
 }
 
-template <typename T, int WMAX, int VEC>
-static void launch_scan(const void* logits, int vocab, int width, const ScanPlan& p, float* pm,
-                        double* ps, float* pv, int* pi, int32_t* err, hipStream_t stream) {
+struct ScanPtrs {
+  float* pm;
+  double* ps;
+  double* pe;  // entropy partials (ENT plans only)
+  float* pv;
+  int* pi;
+};
+
+template <typename T, int WMAX, int VEC, bool ENT>
+static void launch_scan(const void* logits, int vocab, int width, const ScanPlan& p,
+                        const ScanPtrs& w, int32_t* err, hipStream_t stream) {
   if (p.ept == 32)
-    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 32>), dim3(p.chunks, p.rows),
+    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 32, ENT>), dim3(p.chunks, p.rows),
                        dim3(kScanThreads), 0, stream, static_cast<const T*>(logits), vocab,
-                       p.chunks, p.chunk_len, width, pm, ps, pv, pi, err);
+                       p.chunks, p.chunk_len, width, w.pm, w.ps, w.pe, w.pv, w.pi, err);
   else
-    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 128>), dim3(p.chunks, p.rows),
+    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 128, ENT>), dim3(p.chunks, p.rows),
                        dim3(kScanThreads), 0, stream, static_cast<const T*>(logits), vocab,
-                       p.chunks, p.chunk_len, width, pm, ps, pv, pi, err);
+                       p.chunks, p.chunk_len, width, w.pm, w.ps, w.pe, w.pv, w.pi, err);
 }
 
-template <typename T, int WMAX>
-static void scan_vec(const void* logits, int vocab, int width, const ScanPlan& p, float* pm,
-                     double* ps, float* pv, int* pi, int32_t* err, hipStream_t stream) {
+template <typename T, int WMAX, bool ENT>
+static void scan_vec(const void* logits, int vocab, int width, const ScanPlan& p,
+                     const ScanPtrs& w, int32_t* err, hipStream_t stream) {
   constexpr int V = sizeof(T) == 4 ? 4 : 8;
-  if (p.vec == V) launch_scan<T, WMAX, V>(logits, vocab, width, p, pm, ps, pv, pi, err, stream);
-  else launch_scan<T, WMAX, 1>(logits, vocab, width, p, pm, ps, pv, pi, err, stream);
+  if (p.vec == V) launch_scan<T, WMAX, V, ENT>(logits, vocab, width, p, w, err, stream);
+  else launch_scan<T, WMAX, 1, ENT>(logits, vocab, width, p, w, err, stream);
 }
 
-template <typename T>
-static void scan_w(const void* logits, int vocab, int width, const ScanPlan& p, float* pm,
-                   double* ps, float* pv, int* pi, int32_t* err, hipStream_t stream) {
+template <typename T, bool ENT>
+static void scan_w(const void* logits, int vocab, int width, const ScanPlan& p,
+                   const ScanPtrs& w, int32_t* err, hipStream_t stream) {
   switch (p.wmax) {
-    case 1: scan_vec<T, 1>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
-    case 2: scan_vec<T, 2>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
-    case 4: scan_vec<T, 4>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
-    case 8: scan_vec<T, 8>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
-    default: scan_vec<T, 16>(logits, vocab, width, p, pm, ps, pv, pi, err, stream); break;
+    case 1: scan_vec<T, 1, ENT>(logits, vocab, width, p, w, err, stream); break;
+    case 2: scan_vec<T, 2, ENT>(logits, vocab, width, p, w, err, stream); break;
+    case 4: scan_vec<T, 4, ENT>(logits, vocab, width, p, w, err, stream); break;
+    case 8: scan_vec<T, 8, ENT>(logits, vocab, width, p, w, err, stream); break;
+    default: scan_vec<T, 16, ENT>(logits, vocab, width, p, w, err, stream); break;
   }
 }
 
 template <int WMAX>
 static void select_n(int batch, int depth_n, int width, int budget, const ScanPlan& p,
-                     const float* pm, const double* ps, const float* pv, const int* pi,
-                     const int32_t* root_token, int32_t* parent, int32_t* token, int32_t* depth,
-                     double* score, int32_t* n_nodes, int32_t* err, hipStream_t stream) {
+                     const ScanPtrs& w, const int32_t* root_token, int32_t* parent,
+                     int32_t* token, int32_t* depth, double* score, int32_t* n_nodes,
+                     int32_t* err, hipStream_t stream) {
   const SelectLayout L = select_layout(depth_n, width, budget, WMAX);
   if (L.bytes > 64 * 1024)
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&tree_select<WMAX>),
                               hipFuncAttributeMaxDynamicSharedMemorySize,
                               static_cast<int>(L.bytes));
-  hipLaunchKernelGGL((tree_select<WMAX>), dim3(batch), dim3(kSelectThreads), L.bytes, stream, pm,
-                     ps, pv, pi, p.chunks, depth_n, width, budget, L, root_token, parent, token,
-                     depth, score, n_nodes, err);
+  hipLaunchKernelGGL((tree_select<WMAX>), dim3(batch), dim3(kSelectThreads), L.bytes, stream,
+                     w.pm, w.ps, w.pv, w.pi, p.chunks, depth_n, width, budget, L, root_token,
+                     parent, token, depth, score, n_nodes, err);
+}
+
+template <int WMAX>
+static void select_seq_n(int batch, int depth_n, int width, int budget, int expand_mode,
+                         double a, const ScanPlan& p, const ScanPtrs& w,
+                         const int32_t* root_token, int32_t* parent, int32_t* token,
+                         int32_t* depth, double* score, int32_t* n_nodes, int32_t* err,
+                         hipStream_t stream) {
+  hipLaunchKernelGGL((tree_select_seq<WMAX>), dim3(batch), dim3(kSeqThreads), 0, stream, w.pm,
+                     w.ps, w.pe, w.pv, w.pi, p.chunks, depth_n, width, budget, expand_mode, a,
+                     root_token, parent, token, depth, score, n_nodes, err);
+}
+
+// mode < 0: the default build (tree_select); otherwise the variant search.
+static hipError_t build_common(const void* logits, jt_dtype dt, int batch, int depth_n,
+                               int vocab, int width, int budget, int mode, double a,
+                               const int32_t* root_token, int32_t* parent, int32_t* token,
+                               int32_t* depth, double* score, int32_t* n_nodes, int32_t* err,
+                               void* workspace, hipStream_t stream) {
+  const int vec_elems = dt == JT_F32 ? 4 : 8;
+  const bool vec_ok = vocab % vec_elems == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
+  const ScanPlan p = scan_plan(batch, depth_n, vocab, width, vec_ok ? vec_elems : 1);
+  const ScanPlan p1 = scan_plan(batch, depth_n, vocab, width, 1);
+  const ScanWorkspace ws_l = scan_workspace(p1, width);  // sized for the largest plan
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  const ScanPtrs w{reinterpret_cast<float*>(ws + ws_l.off_max),
+                   reinterpret_cast<double*>(ws + ws_l.off_sum),
+                   reinterpret_cast<double*>(ws + ws_l.off_ent),
+                   reinterpret_cast<float*>(ws + ws_l.off_val),
+                   reinterpret_cast<int*>(ws + ws_l.off_idx)};
+  const bool ent = mode >= 0;
+  if (dt == JT_F32) {
+    if (ent) scan_w<float, true>(logits, vocab, width, p, w, err, stream);
+    else scan_w<float, false>(logits, vocab, width, p, w, err, stream);
+  } else {
+    if (ent) scan_w<uint16_t, true>(logits, vocab, width, p, w, err, stream);
+    else scan_w<uint16_t, false>(logits, vocab, width, p, w, err, stream);
+  }
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+#define JT_SELECT(WM)                                                                       \
+  if (mode < 0)                                                                             \
+    select_n<WM>(batch, depth_n, width, budget, p, w, root_token, parent, token, depth, score, \
+                 n_nodes, err, stream);                                                     \
+  else                                                                                      \
+    select_seq_n<WM>(batch, depth_n, width, budget, mode, a, p, w, root_token, parent, token, \
+                     depth, score, n_nodes, err, stream)
+  switch (p.wmax) {
+    case 1: JT_SELECT(1); break;
+    case 2: JT_SELECT(2); break;
+    case 4: JT_SELECT(4); break;
+    case 8: JT_SELECT(8); break;
+    default: JT_SELECT(16); break;
+  }
+#undef JT_SELECT
+  return hipGetLastError();
 }
 
 hipError_t build_tree_launch(const void* logits, jt_dtype dt, int batch, int depth_n, int vocab,
                              int width, int budget, const int32_t* root_token, int32_t* parent,
                              int32_t* token, int32_t* depth, double* score, int32_t* n_nodes,
                              int32_t* err, void* workspace, hipStream_t stream) {
-  const int vec_elems = dt == JT_F32 ? 4 : 8;
-  const bool vec_ok = vocab % vec_elems == 0 && reinterpret_cast<uintptr_t>(logits) % 16 == 0;
-  const ScanPlan p = scan_plan(batch, depth_n, vocab, width, vec_ok ? vec_elems : 1);
-  const ScanPlan p1 = scan_plan(batch, depth_n, vocab, width, 1);
-  const ScanWorkspace w = scan_workspace(p1, width);  // sized for the largest plan
-  unsigned char* ws = static_cast<unsigned char*>(workspace);
-  float* pm = reinterpret_cast<float*>(ws + w.off_max);
-  double* ps = reinterpret_cast<double*>(ws + w.off_sum);
-  float* pv = reinterpret_cast<float*>(ws + w.off_val);
-  int* pi = reinterpret_cast<int*>(ws + w.off_idx);
-  if (dt == JT_F32) scan_w<float>(logits, vocab, width, p, pm, ps, pv, pi, err, stream);
-  else scan_w<uint16_t>(logits, vocab, width, p, pm, ps, pv, pi, err, stream);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  switch (p.wmax) {
-    case 1: select_n<1>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
-    case 2: select_n<2>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
-    case 4: select_n<4>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
-    case 8: select_n<8>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
-    default: select_n<16>(batch, depth_n, width, budget, p, pm, ps, pv, pi, root_token, parent, token, depth, score, n_nodes, err, stream); break;
-  }
-  return hipGetLastError();
+  return build_common(logits, dt, batch, depth_n, vocab, width, budget, -1, 0.0, root_token,
+                      parent, token, depth, score, n_nodes, err, workspace, stream);
+}
+
+hipError_t build_tree_variant_launch(const void* logits, jt_dtype dt, int batch, int depth_n,
+                                     int vocab, int width, int budget, int expand_mode,
+                                     double entropy_weight, const int32_t* root_token,
+                                     int32_t* parent, int32_t* token, int32_t* depth,
+                                     double* score, int32_t* n_nodes, int32_t* err,
+                                     void* workspace, hipStream_t stream) {
+  return build_common(logits, dt, batch, depth_n, vocab, width, budget, expand_mode,
+                      entropy_weight, root_token, parent, token, depth, score, n_nodes, err,
+                      workspace, stream);
 }
 
 }  // namespace jt

@@ -53,6 +53,12 @@ hipError_t accept_stochastic_launch(const void* target, const void* draft, jt_dt
                                     const float* u_sample, int32_t* accept_len,
                                     int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
                                     hipStream_t stream);
+hipError_t build_tree_variant_launch(const void* logits, jt_dtype dt, int batch, int depth_n,
+                                     int vocab, int width, int budget, int expand_mode,
+                                     double entropy_weight, const int32_t* root_token,
+                                     int32_t* parent, int32_t* token, int32_t* depth,
+                                     double* score, int32_t* n_nodes, int32_t* err,
+                                     void* workspace, hipStream_t stream);
 hipError_t commit_kv_launch(void* k_pool, void* v_pool, int elem_bytes, int batch, int hkv,
                             int head_dim, const int32_t* page_table, int max_pages,
                             int num_pages, const int32_t* n_nodes, int max_nodes, int depth_n,
