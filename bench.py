@@ -258,9 +258,84 @@ def main():
         "stage_ms": stage_ms,
         "accept_len": res[0].cpu().tolist(),
     }
+    result["next_rows"] = time_next_rows(B, w, x, tree, d_draft, d_target, d_k, d_v, d_prefix,
+                                         d_table, d_root, ws_build, ws_acc, err, stream)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(w, x, min(args.cpu_seqs, w.batch))
     print(json.dumps(result))
+
+
+def time_next_rows(B, w, x, tree, d_draft, d_target, d_k, d_v, d_prefix, d_table, d_root,
+                   ws_build, ws_acc, err, stream, iters=20):
+    """Average device time (HIP events on the launch stream) of the calls that
+    extend the verify step, on the same batch, after the timed region."""
+    import numpy as np
+    import torch
+    dev = d_draft.device
+    b, T = w.batch, w.max_nodes
+
+    def timed(fn, before=None):
+        fn()  # warm-up
+        tot = 0.0
+        for _ in range(iters):
+            if before is not None:
+                before()
+            e0 = torch.cuda.Event(enable_timing=True)
+            e1 = torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            fn()
+            e1.record(stream)
+            e1.synchronize()
+            tot += e0.elapsed_time(e1)
+        return tot / iters * 1000.0  # us
+
+    par, tok, dep, nn = tree["parent"], tree["token"], tree["depth"], tree["n_nodes"]
+    out = {}
+    # margin acceptance: one pass over the target rows, like the greedy rule
+    us = timed(lambda: B.jt_accept_margin(d_target, w.depth_n, par, tok, dep, nn,
+                                          B.margin_from_ratio(0.5), err=err, workspace=ws_acc))
+    tb = b * T * w.vocab * 4
+    out["accept_margin"] = {"us": us, "target_bytes": tb, "gbps": tb / us / 1e3,
+                            "hbm_frac": tb / us / 1e3 / PEAK_HBM_GBPS}
+    # stochastic verification at T = 1 with seeded uniforms (mostly rejections
+    # on these independent target rows: up to W residual passes per sequence)
+    g = torch.Generator().manual_seed(17)
+    ua = torch.rand((b, T), generator=g).to(dev)
+    usamp = torch.rand((b,), generator=g).to(dev)
+    out["accept_stochastic_us"] = timed(lambda: B.jt_accept_stochastic(
+        d_target, d_draft, par, tok, dep, nn, 1.0, ua, usamp, err=err))
+    # KV commit of each tree's deepest path (prefix_len restored before each call)
+    depth_h, par_h = dep.cpu().numpy(), par.cpu().numpy()
+    anodes = np.full((b, w.depth_n), -1, dtype=np.int32)
+    alen = np.zeros(b, dtype=np.int32)
+    for s_ in range(b):
+        v = int(np.argmax(depth_h[s_][:int(nn[s_])]))
+        path = []
+        while v > 0:
+            path.append(v)
+            v = int(par_h[s_][v])
+        path.reverse()
+        alen[s_] = len(path)
+        anodes[s_, :len(path)] = path
+    d_alen = torch.from_numpy(alen).to(dev)
+    d_anodes = torch.from_numpy(anodes).to(dev)
+    pref = d_prefix.clone()
+    out["commit_kv_us"] = timed(
+        lambda: B.jt_commit_kv(d_k, d_v, d_table, x.num_pages, nn, T, d_alen, d_anodes, pref,
+                               err=err),
+        before=lambda: pref.copy_(d_prefix))
+    out["commit_kv_rows"] = int(alen.sum())
+    # build-mode variants (sequential best-first) next to the default build
+    out["build_default_us"] = timed(lambda: B.jt_build_tree(d_draft, w.width_w, w.budget_b,
+                                                            d_root, err=err, workspace=ws_build))
+    out["build_node_block_us"] = timed(lambda: B.jt_build_tree_variant(
+        d_draft, w.width_w, w.budget_b, d_root, "node_block", 0.0, err=err, workspace=ws_build))
+    out["build_candidate_mixed_us"] = timed(lambda: B.jt_build_tree_variant(
+        d_draft, w.width_w, w.budget_b, d_root, "candidate", 0.5, err=err, workspace=ws_build))
+    torch.cuda.synchronize()
+    if int(err.item()) != 0:
+        raise RuntimeError(f"device error bits {int(err.item())} in the extension calls")
+    return out
 
 
 if __name__ == "__main__":

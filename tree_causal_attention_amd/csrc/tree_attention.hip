@@ -10,9 +10,13 @@
 // in LDS is reused by all the group's query heads and tree nodes.
 //   * The page ids of the item's key range are staged in LDS first, so tile
 //     loads never wait on a page-table lookup.
-//   * K and V of 4 pages (64 keys) are gathered with 16-byte loads one tile
-//     ahead (register staging) and stored row-major [key][dim] in LDS, rows
-//     padded (+16 B for K, +32 B for V) against bank conflicts.
+//   * K and V of 4 pages (64 keys) go from global memory straight into LDS
+//     (global_load_lds_dwordx4, 16 bytes per lane) into a ring of 4 stage
+//     buffers; tile i+2 is fetched while tile i is computed.  Tiles are
+//     row-major [key][dim] with 16-byte chunks XOR-swizzled per key (swz), so
+//     the K fragment reads and the transposing V reads are bank-conflict free
+//     without padding.  Explicit vmcnt waits and one barrier per tile order
+//     the ring (the compiler cannot see the DMA's LDS writes).
 //   * S^T = K Q^T on v_mfma_f32_32x32x16_bf16 (keys as M, queries as N, so
 //     each lane owns one query column and the softmax reductions stay in-lane
 //     plus one cross-half exchange); Q stays in registers.
