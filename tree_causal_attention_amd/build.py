@@ -15,7 +15,7 @@ CSRC = os.path.join(HERE, "csrc")
 OBJ = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libjt.so")
 SOURCES = ["api.hip", "build_tree.hip", "tree_meta.hip", "tree_attention.hip", "accept.hip",
-           "commit.hip", "stochastic.hip"]
+           "commit.hip", "stochastic.hip", "draft_scan.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall",

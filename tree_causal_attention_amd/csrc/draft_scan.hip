@@ -1,0 +1,277 @@
+// draft_row_scan: the per-depth statistics of the tree build (jt_build_tree,
+// jt_build_tree_variant): fp64 log-sum-exp and the top-W tokens of every
+// draft row, and optionally the fp64 entropy partials.
+//
+// Method: JetSpec news piece (mlqm.cn/news/158889), tree-construction
+// paragraph (top-W candidates per depth, scored by log-probability); JetSpec
+// explainer (techwalker.com, "加速AI思考…"), section 五 (the entropy
+// priority the variants rank by).
+//
+// One workgroup per (vocab chunk, depth row) reads its chunk once with 16-byte
+// loads; the partials of a row are merged by the select kernels.
+#include "jt_device.h"
+#include "jt_host.h"
+
+namespace jt {
+
+constexpr int kScanThreads = 256;
+
+template <typename T, int VEC>
+__device__ __forceinline__ void load_vec(const T* x, int i, float (&v)[VEC]) {
+  if constexpr (VEC == 1) {
+    v[0] = load_as_f32(x, i);
+  } else if constexpr (sizeof(T) == 4) {
+    const float4 f = *reinterpret_cast<const float4*>(x + i);
+    v[0] = f.x; v[1] = f.y; v[2] = f.z; v[3] = f.w;
+  } else {
+    const uint4 u = *reinterpret_cast<const uint4*>(x + i);
+    const uint32_t wds[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = __uint_as_float(wds[k] << 16);
+      v[2 * k + 1] = __uint_as_float(wds[k] & 0xFFFF0000u);
+    }
+  }
+}
+
+constexpr int kCandCap = 1024;  // threshold candidates kept per chunk
+
+// One workgroup per (vocab chunk, depth row); thread t holds EPT logits of
+// the chunk in registers (16-byte loads, one pass over HBM).
+//  * max and the fp64 sum of exp(x - max) come straight from the registers;
+//  * top-W: the W-th largest per-thread maximum L is a lower bound of the
+//    chunk's W-th largest logit (W distinct threads hold a value >= L), so
+//    only logits >= L are collected in LDS and ranked; if more than kCandCap
+//    qualify (e.g. massive ties) every thread builds its exact sorted top-W and
+//    W rounds of "best head" merge them.
+// ENT: also the fp64 sum of exp(x - max) * (x - max) (the chunk's entropy
+// partial; tree_select_seq merges it into the per-depth entropy).
+template <typename T, int WMAX, int VEC, int EPT, bool ENT>
+__global__ __launch_bounds__(kScanThreads) void draft_row_scan(
+    const T* __restrict__ logits, int vocab, int chunks, int chunk_len, int width,
+    float* __restrict__ part_max, double* __restrict__ part_sum, double* __restrict__ part_ent,
+    float* __restrict__ part_val, int* __restrict__ part_idx, int32_t* err) {
+  constexpr int NV = EPT / VEC;
+  __shared__ float sm_m[kScanThreads / kWave];
+  __shared__ double sm_s[kScanThreads / kWave];
+  __shared__ double sm_t[kScanThreads / kWave];
+  __shared__ float sm_tmax[kScanThreads];
+  __shared__ float sm_cv[kCandCap];
+  __shared__ int sm_ci[kCandCap];
+  __shared__ int sm_n;
+  __shared__ float sm_L;
+  __shared__ float sm_v[kScanThreads / kWave];
+  __shared__ int sm_i[kScanThreads / kWave];
+
+  const int row = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
+  const int lane = t % kWave, wv = t / kWave;
+  const int begin = c * chunk_len;
+  const int end = min(vocab, begin + chunk_len);
+  const T* x = logits + static_cast<size_t>(row) * vocab;
+
+  float xv[EPT];
+  bool bad = false;
+  float m = -INFINITY;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = begin + (j * kScanThreads + t) * VEC;
+    float v[VEC];
+    if (i < end) {
+      load_vec<T, VEC>(x, i, v);
+    } else {
+#pragma unroll
+      for (int e = 0; e < VEC; ++e) v[e] = -INFINITY;
+    }
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      float y = v[e];
+      if (y != y || y == INFINITY) { bad = true; y = -INFINITY; }
+      xv[j * VEC + e] = y;
+      m = fmaxf(m, y);
+    }
+  }
+  if (bad) report(err, JT_DERR_BAD_LOGIT);
+  if (t == 0) sm_n = 0;
+
+  // ---- chunk max
+  float wm = m;
+  for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, shfl_xor(wm, o));
+  if (lane == 0) sm_m[wv] = wm;
+  sm_tmax[t] = m;
+  __syncthreads();
+  float M = sm_m[0];
+  for (int w = 1; w < kScanThreads / kWave; ++w) M = fmaxf(M, sm_m[w]);
+
+  // ---- fp64 sum of exp(x - M) over the registers
+  double sacc = 0.0, tacc = 0.0;
+  if (M != -INFINITY) {
+    const double Md = static_cast<double>(M);
+#pragma unroll
+    for (int k = 0; k < EPT; ++k) {
+      const double dx = static_cast<double>(fmaxf(xv[k], -1.0e30f)) - Md;
+      const double e = exp(dx);
+      const bool fin = xv[k] != -INFINITY;
+      sacc += fin ? e : 0.0;
+      if constexpr (ENT) tacc += fin ? e * dx : 0.0;
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) sacc += shfl_xor_f64(sacc, o);
+  if (lane == 0) sm_s[wv] = sacc;
+  if constexpr (ENT) {
+    for (int o = 32; o > 0; o >>= 1) tacc += shfl_xor_f64(tacc, o);
+    if (lane == 0) sm_t[wv] = tacc;
+  }
+
+  // ---- threshold: the W-th largest thread maximum (ties by thread id)
+  int rank = 0;
+  for (int u = 0; u < kScanThreads; ++u) {
+    const float mu = sm_tmax[u];
+    rank += (mu > m || (mu == m && u < t)) ? 1 : 0;
+  }
+  if (rank == width - 1) sm_L = m;
+  __syncthreads();
+  if (t == 0) {
+    double S = 0.0;
+    for (int w = 0; w < kScanThreads / kWave; ++w) S += sm_s[w];
+    part_max[row * chunks + c] = M;
+    part_sum[row * chunks + c] = S;
+    if constexpr (ENT) {
+      double Tt = 0.0;
+      for (int w = 0; w < kScanThreads / kWave; ++w) Tt += sm_t[w];
+      part_ent[row * chunks + c] = Tt;
+    }
+  }
+  const float L = sm_L;
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+    const int i = begin + (j * kScanThreads + t) * VEC;
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      if (i + e < end && xv[j * VEC + e] >= L) {
+        const int pos = atomicAdd(&sm_n, 1);
+        if (pos < kCandCap) { sm_cv[pos] = xv[j * VEC + e]; sm_ci[pos] = i + e; }
+      }
+    }
+  }
+  __syncthreads();
+  const int nc = sm_n;
+  const size_t out0 = (static_cast<size_t>(row) * chunks + c) * width;
+  if (nc <= kCandCap) {
+    for (int q = t; q < nc; q += kScanThreads) {
+      const float vq = sm_cv[q];
+      const int iq = sm_ci[q];
+      int r = 0;
+      for (int u = 0; u < nc; ++u) r += better(sm_cv[u], sm_ci[u], vq, iq) ? 1 : 0;
+      if (r < width) { part_val[out0 + r] = vq; part_idx[out0 + r] = iq; }
+    }
+    for (int r = nc + t; r < width; r += kScanThreads) {
+      part_val[out0 + r] = -INFINITY;
+      part_idx[out0 + r] = INT32_MAX;
+    }
+    return;
+  }
+
+  // ---- overflow: exact per-thread sorted lists, merged by W rounds
+  float tv[WMAX];
+  int ti[WMAX];
+#pragma unroll
+  for (int k = 0; k < WMAX; ++k) { tv[k] = -INFINITY; ti[k] = INT32_MAX; }
+#pragma unroll
+  for (int j = 0; j < NV; ++j) {
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const int i = begin + (j * kScanThreads + t) * VEC + e;
+      const float y = xv[j * VEC + e];
+      if (i < end && better(y, i, tv[WMAX - 1], ti[WMAX - 1])) {
+        // Sorted insert as a select network: slot k keeps its entry if it
+        // precedes the new one, takes the new one at the first slot it beats,
+        // and takes its predecessor's entry after that.  Slots are rewritten
+        // from the last one up, so slot k-1 still holds its old entry.
+#pragma unroll
+        for (int k = WMAX - 1; k >= 0; --k) {
+          const int u = k > 0 ? k - 1 : 0;
+          const bool b = better(y, i, tv[k], ti[k]);
+          const bool b_up = k > 0 && better(y, i, tv[u], ti[u]);
+          const float up_v = tv[u];
+          const int up_i = ti[u];
+          tv[k] = b ? (b_up ? up_v : y) : tv[k];
+          ti[k] = b ? (b_up ? up_i : i) : ti[k];
+        }
+      }
+    }
+  }
+  for (int r = 0; r < width; ++r) {
+    float bv = tv[0];
+    int bi = ti[0];
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ov = shfl_xor(bv, o);
+      const int oi = shfl_xor(bi, o);
+      if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
+    }
+    __syncthreads();  // previous round's readers are done with sm_v/sm_i
+    if (lane == 0) { sm_v[wv] = bv; sm_i[wv] = bi; }
+    __syncthreads();
+    float gv = sm_v[0];
+    int gi = sm_i[0];
+    for (int w = 1; w < kScanThreads / kWave; ++w)
+      if (better(sm_v[w], sm_i[w], gv, gi)) { gv = sm_v[w]; gi = sm_i[w]; }
+    if (t == 0) { part_val[out0 + r] = gv; part_idx[out0 + r] = gi; }
+    if (ti[0] == gi && gi != INT32_MAX) {
+#pragma unroll
+      for (int k = 0; k + 1 < WMAX; ++k) { tv[k] = tv[k + 1]; ti[k] = ti[k + 1]; }
+      tv[WMAX - 1] = -INFINITY;
+      ti[WMAX - 1] = INT32_MAX;
+    }
+  }
+}
+
+
+// ------------------------------------------------------------------ host side
+
+template <typename T, int WMAX, int VEC, bool ENT>
+static void launch_scan(const void* logits, int vocab, int width, const ScanArgs& a,
+                        hipStream_t stream) {
+  const dim3 grid(a.chunks, a.rows);
+  if (a.ept == 32)
+    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 32, ENT>), grid, dim3(kScanThreads), 0,
+                       stream, static_cast<const T*>(logits), vocab, a.chunks, a.chunk_len,
+                       width, a.pm, a.ps, a.pe, a.pv, a.pi, a.err);
+  else
+    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 128, ENT>), grid, dim3(kScanThreads), 0,
+                       stream, static_cast<const T*>(logits), vocab, a.chunks, a.chunk_len,
+                       width, a.pm, a.ps, a.pe, a.pv, a.pi, a.err);
+}
+
+template <typename T, int WMAX, bool ENT>
+static void scan_vec(const void* logits, int vocab, int width, const ScanArgs& a,
+                     hipStream_t stream) {
+  constexpr int V = sizeof(T) == 4 ? 4 : 8;
+  if (a.vec == V) launch_scan<T, WMAX, V, ENT>(logits, vocab, width, a, stream);
+  else launch_scan<T, WMAX, 1, ENT>(logits, vocab, width, a, stream);
+}
+
+template <typename T, bool ENT>
+static void scan_w(const void* logits, int vocab, int width, const ScanArgs& a,
+                   hipStream_t stream) {
+  switch (a.wmax) {
+    case 1: scan_vec<T, 1, ENT>(logits, vocab, width, a, stream); break;
+    case 2: scan_vec<T, 2, ENT>(logits, vocab, width, a, stream); break;
+    case 4: scan_vec<T, 4, ENT>(logits, vocab, width, a, stream); break;
+    case 8: scan_vec<T, 8, ENT>(logits, vocab, width, a, stream); break;
+    default: scan_vec<T, 16, ENT>(logits, vocab, width, a, stream); break;
+  }
+}
+
+hipError_t draft_scan_launch(const void* logits, jt_dtype dt, bool ent, int vocab, int width,
+                             const ScanArgs& a, hipStream_t stream) {
+  if (dt == JT_F32) {
+    if (ent) scan_w<float, true>(logits, vocab, width, a, stream);
+    else scan_w<float, false>(logits, vocab, width, a, stream);
+  } else {
+    if (ent) scan_w<uint16_t, true>(logits, vocab, width, a, stream);
+    else scan_w<uint16_t, false>(logits, vocab, width, a, stream);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace jt

@@ -11,6 +11,19 @@
 
 namespace jt {
 
+// draft_scan.hip: per-(row, chunk) partials of the draft rows
+struct ScanArgs {
+  int rows, chunks, chunk_len, ept, vec, wmax;
+  float* pm;   // chunk max            [rows * chunks]
+  double* ps;  // sum exp(x - max)     [rows * chunks]
+  double* pe;  // sum exp(x - max)(x - max), only with ent
+  float* pv;   // chunk top-W values   [rows * chunks * width]
+  int* pi;     // chunk top-W token ids
+  int32_t* err;
+};
+hipError_t draft_scan_launch(const void* logits, jt_dtype dt, bool ent, int vocab, int width,
+                             const ScanArgs& a, hipStream_t stream);
+
 // build_tree.hip
 size_t build_tree_workspace_bytes(int batch, int depth_n, int vocab, int width);
 size_t build_tree_lds_bytes(int depth_n, int width, int budget);
