@@ -217,7 +217,9 @@ static ArgmaxPlan argmax_plan(int batch, int max_nodes, int vocab, int vec_elems
   const long long rows = static_cast<long long>(batch) * max_nodes;
   const int by_rows = static_cast<int>(std::max<long long>(1, (2048 + rows - 1) / std::max<long long>(1, rows)));
   const int by_vocab = std::max(1, (vocab + 4095) / 4096);
-  p.chunks = std::min(64, std::min(by_rows, by_vocab));
+  // at least 8 chunks per row: with one workgroup per row the last few rows
+  // run alone after the rest and stream at one workgroup's memory parallelism
+  p.chunks = std::min(64, std::min(std::max(by_rows, 8), by_vocab));
   p.vec = (vocab % vec_elems == 0) ? vec_elems : 1;
   int len = (vocab + p.chunks - 1) / p.chunks;
   len = (len + p.vec - 1) / p.vec * p.vec;

@@ -39,11 +39,11 @@ constexpr int kCandCap = 1024;  // threshold candidates kept per chunk
 // One workgroup per (vocab chunk, depth row); thread t holds EPT logits of
 // the chunk in registers (16-byte loads, one pass over HBM).
 //  * max and the fp64 sum of exp(x - max) come straight from the registers;
-//  * top-W: the W-th largest per-thread maximum L is a lower bound of the
-//    chunk's W-th largest logit (W distinct threads hold a value >= L), so
-//    only logits >= L are collected in LDS and ranked; if more than kCandCap
-//    qualify (e.g. massive ties) every thread builds its exact sorted top-W and
-//    W rounds of "best head" merge them.
+//  * top-W: each wave offers its ceil(WMAX/4) largest lane maxima (distinct
+//    logits of the chunk); the W-th largest offer L is a lower bound of the
+//    chunk's W-th largest logit, so only logits >= L are collected in LDS and
+//    ranked; if more than kCandCap qualify (e.g. massive ties) every thread
+//    builds its exact sorted top-W and W rounds of "best head" merge them.
 // ENT: also the fp64 sum of exp(x - max) * (x - max) (the chunk's entropy
 // partial; tree_select_seq merges it into the per-depth entropy).
 template <typename T, int WMAX, int VEC, int EPT, bool ENT>
@@ -55,7 +55,8 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   __shared__ float sm_m[kScanThreads / kWave];
   __shared__ double sm_s[kScanThreads / kWave];
   __shared__ double sm_t[kScanThreads / kWave];
-  __shared__ float sm_tmax[kScanThreads];
+  constexpr int PW = (WMAX + 3) / 4;  // threshold offers per wave
+  __shared__ float sm_off[(kScanThreads / kWave) * PW];
   __shared__ float sm_cv[kCandCap];
   __shared__ int sm_ci[kCandCap];
   __shared__ int sm_n;
@@ -97,7 +98,21 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   float wm = m;
   for (int o = 32; o > 0; o >>= 1) wm = fmaxf(wm, shfl_xor(wm, o));
   if (lane == 0) sm_m[wv] = wm;
-  sm_tmax[t] = m;
+  {
+    // the wave's PW largest lane maxima (ties to the lower lane), one per round
+    bool taken = false;
+    for (int r = 0; r < PW; ++r) {
+      float bv = taken ? -INFINITY : m;
+      int bl = taken ? kWave : lane;  // taken lanes lose every comparison
+      for (int o = 32; o > 0; o >>= 1) {
+        const float ov = shfl_xor(bv, o);
+        const int ol = shfl_xor(bl, o);
+        if (ov > bv || (ov == bv && ol < bl)) { bv = ov; bl = ol; }
+      }
+      if (lane == bl) taken = true;
+      if (lane == 0) sm_off[wv * PW + r] = bl < kWave ? bv : -INFINITY;
+    }
+  }
   __syncthreads();
   float M = sm_m[0];
   for (int w = 1; w < kScanThreads / kWave; ++w) M = fmaxf(M, sm_m[w]);
@@ -122,13 +137,16 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
     if (lane == 0) sm_t[wv] = tacc;
   }
 
-  // ---- threshold: the W-th largest thread maximum (ties by thread id)
-  int rank = 0;
-  for (int u = 0; u < kScanThreads; ++u) {
-    const float mu = sm_tmax[u];
-    rank += (mu > m || (mu == m && u < t)) ? 1 : 0;
+  // ---- threshold: the W-th largest of the 4 * PW offers (ties by position)
+  if (t < (kScanThreads / kWave) * PW) {
+    const float v = sm_off[t];
+    int rank = 0;
+    for (int u = 0; u < (kScanThreads / kWave) * PW; ++u) {
+      const float ou = sm_off[u];
+      rank += (ou > v || (ou == v && u < t)) ? 1 : 0;
+    }
+    if (rank == width - 1) sm_L = v;
   }
-  if (rank == width - 1) sm_L = m;
   __syncthreads();
   if (t == 0) {
     double S = 0.0;
