@@ -367,15 +367,20 @@ jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int n
  *             JT_DERR_BAD_NNODES, JT_DERR_BAD_PARENT, JT_DERR_BAD_DEPTH,
  *             JT_DERR_BAD_TOKEN, JT_DERR_BAD_UNIFORM (that sequence's outputs
  *             are then zero / -1).
+ *   workspace  jt_accept_stochastic_workspace(batch, vocab) bytes (2 * vocab
+ *             doubles per sequence: the exponentials of the current target
+ *             row and of the children's draft row, reused by every pass).
  * Limits: batch >= 0, 1 <= max_nodes <= 1024, vocab >= 1, 1 <= depth_n <= 64.
- * One workgroup per sequence; no workspace.
+ * One workgroup per sequence.
  * ---------------------------------------------------------------------- */
+size_t jt_accept_stochastic_workspace(int batch, int vocab);
 jt_status jt_accept_stochastic(const void* target_logits, const void* draft_logits, jt_dtype dt,
                                int batch, int max_nodes, int vocab, int depth_n,
                                const int32_t* parent, const int32_t* token, const int32_t* depth,
                                const int32_t* n_nodes, float temperature, const float* u_accept,
                                const float* u_sample, int32_t* accept_len, int32_t* accept_nodes,
-                               int32_t* bonus_token, int32_t* err, void* stream);
+                               int32_t* bonus_token, int32_t* err, void* workspace,
+                               size_t workspace_bytes, void* stream);
 
 #ifdef __cplusplus
 }

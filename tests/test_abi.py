@@ -157,8 +157,11 @@ def test_accept_stochastic_validation(lib):
     f = lib.jt_accept_stochastic
     p = ctypes.c_void_p(1)
 
-    def call(temp=0.7, dt=1, b=1, T=17, V=100, N=4, ua=p):
-        return f(p, p, dt, b, T, V, N, p, p, p, p, temp, ua, p, p, p, p, None, None)
+    need = lib.jt_accept_stochastic_workspace(1, 100)
+    assert need == 2 * 100 * 8
+
+    def call(temp=0.7, dt=1, b=1, T=17, V=100, N=4, ua=p, ws=need):
+        return f(p, p, dt, b, T, V, N, p, p, p, p, temp, ua, p, p, p, p, None, p, ws, None)
 
     assert call(temp=0.0) == B.JT_ERR_INVALID_ARG
     assert call(temp=-1.0) == B.JT_ERR_INVALID_ARG
@@ -168,6 +171,7 @@ def test_accept_stochastic_validation(lib):
     assert call(N=65) == B.JT_ERR_UNSUPPORTED
     assert call(T=1025) == B.JT_ERR_UNSUPPORTED
     assert call(ua=None) == B.JT_ERR_INVALID_ARG
+    assert call(ws=need - 1) == B.JT_ERR_WORKSPACE
     assert call(b=0) == B.JT_OK
 
 

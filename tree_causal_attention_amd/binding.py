@@ -47,8 +47,10 @@ SIGNATURES = {
                                   ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
     "jt_commit_kv": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
                               _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
+    "jt_accept_stochastic_workspace": (_c_size, [_c_int, _c_int]),
     "jt_accept_stochastic": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
-                                      _vp, _vp, _c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+                                      _vp, _vp, _c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
+                                      _vp]),
 }
 
 
@@ -254,7 +256,7 @@ def jt_commit_kv(k_pool, v_pool, page_table, num_pages, n_nodes, max_nodes: int,
 
 
 def jt_accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes,
-                         temperature: float, u_accept, u_sample, err=None):
+                         temperature: float, u_accept, u_sample, err=None, workspace=None):
     """Lossless verification at temperature T > 0 with caller-supplied uniforms.
 
     u_accept [b, max_nodes] f32, u_sample [b] f32, all in [0, 1).
@@ -277,8 +279,11 @@ def jt_accept_stochastic(target_logits, draft_logits, parent, token, depth, n_no
     alen = torch.empty((b,), dtype=torch.int32, device=dev)
     anodes = torch.empty((b, depth_n), dtype=torch.int32, device=dev)
     bonus = torch.empty((b,), dtype=torch.int32, device=dev)
+    ws = workspace if workspace is not None else _workspace(
+        lib.jt_accept_stochastic_workspace(b, V), dev)
     _check("jt_accept_stochastic", lib.jt_accept_stochastic(
         _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), b, T, V, depth_n,
         _ptr(parent), _ptr(token), _ptr(depth), _ptr(n_nodes), float(temperature), _ptr(u_accept),
-        _ptr(u_sample), _ptr(alen), _ptr(anodes), _ptr(bonus), _ptr(err), _stream()))
+        _ptr(u_sample), _ptr(alen), _ptr(anodes), _ptr(bonus), _ptr(err), _ptr(ws), ws.numel(),
+        _stream()))
     return alen, anodes, bonus

@@ -223,12 +223,18 @@ jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int n
                                        prefix_len, err, static_cast<hipStream_t>(stream)));
 }
 
+size_t jt_accept_stochastic_workspace(int batch, int vocab) {
+  if (batch <= 0 || vocab < 1) return 0;
+  return jt::accept_stochastic_workspace_bytes(batch, vocab);
+}
+
 jt_status jt_accept_stochastic(const void* target_logits, const void* draft_logits, jt_dtype dt,
                                int batch, int max_nodes, int vocab, int depth_n,
                                const int32_t* parent, const int32_t* token, const int32_t* depth,
                                const int32_t* n_nodes, float temperature, const float* u_accept,
                                const float* u_sample, int32_t* accept_len, int32_t* accept_nodes,
-                               int32_t* bonus_token, int32_t* err, void* stream) {
+                               int32_t* bonus_token, int32_t* err, void* workspace,
+                               size_t workspace_bytes, void* stream) {
   if (batch < 0 || max_nodes < 1 || vocab < 1 || depth_n < 1 || !valid_dtype(dt))
     return JT_ERR_INVALID_ARG;
   if (!(temperature > 0.0f) || !std::isfinite(temperature)) return JT_ERR_INVALID_ARG;
@@ -237,10 +243,12 @@ jt_status jt_accept_stochastic(const void* target_logits, const void* draft_logi
   if (!target_logits || !draft_logits || !parent || !token || !depth || !n_nodes || !u_accept ||
       !u_sample || !accept_len || !accept_nodes || !bonus_token)
     return JT_ERR_INVALID_ARG;
+  const size_t need = jt::accept_stochastic_workspace_bytes(batch, vocab);
+  if (!workspace || workspace_bytes < need) return JT_ERR_WORKSPACE;
   return launched(jt::accept_stochastic_launch(
       target_logits, draft_logits, dt, batch, max_nodes, vocab, depth_n, parent, token, depth,
       n_nodes, temperature, u_accept, u_sample, accept_len, accept_nodes, bonus_token, err,
-      static_cast<hipStream_t>(stream)));
+      workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -65,7 +65,8 @@ hipError_t accept_stochastic_launch(const void* target, const void* draft, jt_dt
                                     float temperature, const float* u_accept,
                                     const float* u_sample, int32_t* accept_len,
                                     int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
-                                    hipStream_t stream);
+                                    void* workspace, hipStream_t stream);
+size_t accept_stochastic_workspace_bytes(int batch, int vocab);
 hipError_t build_tree_variant_launch(const void* logits, jt_dtype dt, int batch, int depth_n,
                                      int vocab, int width, int budget, int expand_mode,
                                      double entropy_weight, const int32_t* root_token,

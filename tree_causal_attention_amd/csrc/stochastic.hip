@@ -9,11 +9,17 @@
 // candidate rank) are tried in turn with q = softmax(draft row depth / T) of
 // their depth: child v (token x) is accepted iff u_accept[v] * q(x) < p(x);
 // a rejection replaces p by norm(max(0, p - q)).  With q fixed inside one
-// node's child list, after k rejections p_k = max(0, p - s_k q) / N_k with
-// s_0 = 0, N_0 = 1, s_k = s_{k-1} + N_{k-1} and
-// N_k = sum_y max(0, p(y) - s_k q(y)), so each rejection costs one fp64 pass
-// over the vocabulary.  When no child is accepted the bonus token is the
-// inverse-CDF draw of u_sample from the current p.  All probability
+// node's child list, k rejections leave p_k proportional to
+// max(0, p - s_k q), s_0 = 0, s_{k+1} = s_k + sum_y max(0, p - s_k q).
+// The kernel keeps that in unnormalised form: with et = exp((x - max) / T)
+// of the target row (sum zt), ed the same for the draft row (sum zd) and
+// c = s zt / zd, the residual weights are max(0, et - c ed), their sum U, and
+// a rejection sets c += U / zd.  The accept test reads
+//   u_accept * ed[x] / zd < max(0, et[x] - c ed[x]) / U,
+// the same inequality as u q(x) < p_k(x) up to rounding.  et and ed are kept
+// in the workspace, so every pass after the row statistics is one fused
+// multiply-add per entry.  When no child is accepted the bonus token is the
+// inverse-CDF draw of u_sample over the residual weights.  All probability
 // arithmetic is fp64 (exp from the device math library).
 #include "jt_device.h"
 #include "jt_host.h"
@@ -63,11 +69,13 @@ __device__ __forceinline__ int block_or(int v, int* red) {
   return t;
 }
 
-// Row statistics: max (exact) and Z = sum exp((x - max) / T) in fp64.  Sets
+// Row statistics: max (exact) and Z = sum exp((x - max) / T) in fp64; every
+// exp((x - max) / T) is also stored in e_out[i] for the later passes.  Sets
 // *bad for NaN / +inf entries or a row without a finite entry.
 template <typename T>
 __device__ void row_stats(RowView<T> r, int vocab, double tinv, float* m_out, double* z_out,
-                          bool* bad, float* redf, double* redd, int* redi) {
+                          bool* bad, double* __restrict__ e_out, float* redf, double* redd,
+                          int* redi) {
   float m = -INFINITY;
   int b = 0;
   for (int i = threadIdx.x; i < vocab; i += kStThreads) {
@@ -79,9 +87,12 @@ __device__ void row_stats(RowView<T> r, int vocab, double tinv, float* m_out, do
   b = block_or(b, redi);
   double z = 0.0;
   if (!b && m != -INFINITY)
-    for (int i = threadIdx.x; i < vocab; i += kStThreads)
-      z += exp((static_cast<double>(r.at(i)) - static_cast<double>(m)) * tinv);
-  z = block_sum(z, redd);
+    for (int i = threadIdx.x; i < vocab; i += kStThreads) {
+      const double e = exp((static_cast<double>(r.at(i)) - static_cast<double>(m)) * tinv);
+      e_out[i] = e;
+      z += e;
+    }
+  z = block_sum(z, redd);  // its barriers also publish e_out to the workgroup
   *m_out = m;
   *z_out = z;
   *bad = b || m == -INFINITY;
@@ -94,19 +105,22 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
     const int32_t* __restrict__ depth, const int32_t* __restrict__ n_nodes, float temperature,
     const float* __restrict__ u_accept, const float* __restrict__ u_sample,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
-    int32_t* __restrict__ bonus_token, int32_t* err) {
+    int32_t* __restrict__ bonus_token, int32_t* err, double* __restrict__ ecache) {
   __shared__ int par[1024];
-  __shared__ float dmax[64];
-  __shared__ double dz[64];
-  __shared__ int dstate[64];  // 0 unknown, 1 valid, 2 bad
   __shared__ float redf[kStWaves];
   __shared__ double redd[kStWaves];
   __shared__ int redi[kStWaves];
-  __shared__ double chunk_pre[kStThreads];
+  __shared__ double wsum[kStWaves], wpre[kStWaves];
   __shared__ int path[64];
+  __shared__ int pick;
+  __shared__ double thr_s;
   const int seq = blockIdx.x, tid = threadIdx.x;
+  const int lane = tid % kWave, wv = tid / kWave;
   const int n = n_nodes[seq];
   int32_t* nodes_out = accept_nodes + static_cast<size_t>(seq) * depth_n;
+  // exp((x - max) / T) of the current target row and of the children's draft row
+  double* et = ecache + static_cast<size_t>(seq) * 2 * vocab;
+  double* ed = et + vocab;
   auto fail = [&](int bits) {
     if (tid == 0) {
       report(err, bits);
@@ -138,115 +152,99 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
     const float us = u_sample[seq];
     if (!(us >= 0.0f && us < 1.0f)) b |= JT_DERR_BAD_UNIFORM;
   }
-  for (int k = tid; k < 64; k += kStThreads) dstate[k] = 0;
   b = block_or(b, redi);
   if (b) { fail(b); return; }
 
   const double tinv = 1.0 / static_cast<double>(temperature);
   const T* draft_seq = draft + static_cast<size_t>(seq) * depth_n * vocab;
   int u = 0, L = 0;
-  // current distribution: p_cur(y) = max(0, p(y) - s q(y)) / N over the
-  // current node's target row (q of the children's depth; s = 0: plain p)
+  // current distribution: weights max(0, et - c ed) over the current node's
+  // target row (ed: the children's draft row), total U; c = 0 is plain p
   float mt = 0.0f, md = 0.0f;
-  double zt = 1.0, zd = 1.0, s = 0.0, N = 1.0;
-  int qdepth = 0;  // draft row of q (1-based depth), 0: no q term
+  double zt = 1.0, zd = 1.0, c = 0.0, U = 1.0;
   while (true) {
     bool bad = false;
-    RowView<T> tr{target + (base + u) * vocab};
-    row_stats(tr, vocab, tinv, &mt, &zt, &bad, redf, redd, redi);
+    row_stats(RowView<T>{target + (base + u) * vocab}, vocab, tinv, &mt, &zt, &bad, et, redf,
+              redd, redi);
     if (bad) { fail(JT_DERR_BAD_LOGIT); return; }
-    s = 0.0;
-    N = 1.0;
-    qdepth = 0;
+    c = 0.0;
+    U = zt;
+    bool have_q = false;  // ed holds the children's draft row (all at depth(u) + 1)
     int next = -1;
     for (int v = u + 1; v < n; ++v) {
       if (par[v] != u) continue;  // uniform: par is in LDS, v is uniform
-      const int d = depth[base + v];
-      if (dstate[d - 1] == 0) {
-        RowView<T> dr{draft_seq + static_cast<size_t>(d - 1) * vocab};
-        float m;
-        double z;
-        row_stats(dr, vocab, tinv, &m, &z, &bad, redf, redd, redi);
-        __syncthreads();
-        if (tid == 0) {
-          dmax[d - 1] = m;
-          dz[d - 1] = z;
-          dstate[d - 1] = bad ? 2 : 1;
-        }
-        __syncthreads();
+      if (!have_q) {
+        const int d = depth[base + v];
+        row_stats(RowView<T>{draft_seq + static_cast<size_t>(d - 1) * vocab}, vocab, tinv, &md,
+                  &zd, &bad, ed, redf, redd, redi);
+        if (bad) { fail(JT_DERR_BAD_LOGIT); return; }
+        have_q = true;
       }
-      if (dstate[d - 1] == 2) { fail(JT_DERR_BAD_LOGIT); return; }
-      md = dmax[d - 1];
-      zd = dz[d - 1];
-      qdepth = d;
-      const T* drow = draft_seq + static_cast<size_t>(d - 1) * vocab;
       const int x = token[base + v];
-      const double px = exp((static_cast<double>(load_as_f32(tr.row, x)) - mt) * tinv) / zt;
-      const double qx = exp((static_cast<double>(load_as_f32(drow, x)) - md) * tinv) / zd;
-      const double pcur = fmax(0.0, px - s * qx) / N;
+      const double qx = ed[x] / zd;
+      const double pcur = fmax(0.0, et[x] - c * ed[x]) / U;
       if (static_cast<double>(u_accept[base + v]) * qx < pcur) {
         next = v;
         break;
       }
-      // rejection: N_new = sum_y max(0, p(y) - (s + N) q(y))
-      const double s_new = s + N;
+      // rejection: c' = c + U / zd, U' = sum_y max(0, et - c' ed)
+      const double c_new = c + U / zd;
       double part = 0.0;
-      for (int i = tid; i < vocab; i += kStThreads) {
-        const double py = exp((static_cast<double>(tr.at(i)) - mt) * tinv) / zt;
-        const double qy = exp((static_cast<double>(load_as_f32(drow, i)) - md) * tinv) / zd;
-        part += fmax(0.0, py - s_new * qy);
-      }
-      const double nn = block_sum(part, redd);
-      if (nn == 0.0) break;  // no mass left: keep the previous distribution
-      s = s_new;
-      N = nn;
+      for (int i = tid; i < vocab; i += kStThreads) part += fmax(0.0, et[i] - c_new * ed[i]);
+      const double un = block_sum(part, redd);
+      if (un == 0.0) break;  // no mass left: keep the previous distribution
+      c = c_new;
+      U = un;
     }
     if (next < 0) break;
     if (tid == 0) path[L] = next;
     ++L;
     u = next;
+    __syncthreads();  // every thread is done with et before the next row overwrites it
   }
-  // ---- bonus: inverse-CDF draw from p_cur over the current node's row
-  const T* trow = target + (base + u) * vocab;
-  const T* drow = qdepth > 0 ? draft_seq + static_cast<size_t>(qdepth - 1) * vocab : nullptr;
-  const int chunk = (vocab + kStThreads - 1) / kStThreads;
-  const int lo = min(vocab, tid * chunk), hi = min(vocab, lo + chunk);
-  auto weight = [&](int i) -> double {
-    const double py = exp((static_cast<double>(load_as_f32(trow, i)) - mt) * tinv) / zt;
-    if (s == 0.0) return py;
-    const double qy = exp((static_cast<double>(load_as_f32(drow, i)) - md) * tinv) / zd;
-    return fmax(0.0, py - s * qy);
-  };
+  // ---- bonus: inverse-CDF draw over the residual weights of the current node.
+  // Wave w owns a contiguous segment of the vocabulary (lanes read it
+  // coalesced); segment sums give an exclusive prefix, and the wave whose
+  // interval holds u * total scans its segment 64 entries at a time.
+  auto weight = [&](int i) -> double { return c == 0.0 ? et[i] : fmax(0.0, et[i] - c * ed[i]); };
+  const int seg = (vocab + kStWaves * kWave - 1) / (kStWaves * kWave) * kWave;
+  const int s0 = min(vocab, wv * seg), s1 = min(vocab, s0 + seg);
   double own = 0.0;
-  for (int i = lo; i < hi; ++i) own += weight(i);
-  chunk_pre[tid] = own;
+  for (int i = s0 + lane; i < s1; i += kWave) own += weight(i);
+  for (int o = 32; o > 0; o >>= 1) own += __shfl_xor(own, o, kWave);
+  if (lane == 0) wsum[wv] = own;
   __syncthreads();
-  __shared__ int pick;
-  __shared__ double thr_s;
   if (tid == 0) {
     double tot = 0.0;
-    for (int k = 0; k < kStThreads; ++k) {
-      const double c = chunk_pre[k];
-      chunk_pre[k] = tot;  // exclusive prefix
-      tot += c;
+    for (int k = 0; k < kStWaves; ++k) {
+      wpre[k] = tot;  // exclusive prefix
+      tot += wsum[k];
     }
     thr_s = static_cast<double>(u_sample[seq]) * tot;
     pick = -1;
   }
   __syncthreads();
   const double thr = thr_s;
-  // The chunk intervals [pre_k, pre_k + own_k) tile [0, tot) exactly (the
-  // same fp64 additions as the prefix), so exactly one thread owns thr.
-  if (lo < hi && chunk_pre[tid] <= thr && chunk_pre[tid] + own > thr) {
-    double run = chunk_pre[tid];
+  // The intervals [wpre_k, wpre_k + wsum_k) tile [0, tot) exactly (the same
+  // fp64 additions as the prefix), so exactly one wave owns thr.
+  if (s0 < s1 && wpre[wv] <= thr && wpre[wv] + wsum[wv] > thr) {
+    double carry = wpre[wv];
     int y = -1, last_pos = -1;
-    for (int i = lo; i < hi; ++i) {
-      const double wi = weight(i);
-      if (wi > 0.0) last_pos = i;
-      run += wi;
-      if (run > thr) { y = i; break; }
+    for (int r0 = s0; r0 < s1 && y < 0; r0 += kWave) {
+      const int i = r0 + lane;
+      const double w = i < s1 ? weight(i) : 0.0;
+      double incl = w;  // inclusive prefix over the 64 lanes
+      for (int o = 1; o < kWave; o <<= 1) {
+        const double up = __shfl_up(incl, o, kWave);
+        if (lane >= o) incl += up;
+      }
+      const unsigned long long hit = __ballot(carry + incl > thr);
+      const unsigned long long pos = __ballot(w > 0.0);
+      if (pos) last_pos = r0 + 63 - __clzll(pos);
+      if (hit) y = r0 + __ffsll(static_cast<long long>(hit)) - 1;
+      carry += __shfl(incl, kWave - 1, kWave);
     }
-    pick = y >= 0 ? y : last_pos;  // re-summation rounding: last positive weight of the chunk
+    if (lane == 0) pick = y >= 0 ? y : last_pos;  // re-summation rounding: last positive weight
   }
   __syncthreads();
   if (tid == 0) {
@@ -256,6 +254,10 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
   }
 }
 
+size_t accept_stochastic_workspace_bytes(int batch, int vocab) {
+  return static_cast<size_t>(batch) * 2 * vocab * sizeof(double);
+}
+
 hipError_t accept_stochastic_launch(const void* target, const void* draft, jt_dtype dt,
                                     int batch, int max_nodes, int vocab, int depth_n,
                                     const int32_t* parent, const int32_t* token,
@@ -263,18 +265,19 @@ hipError_t accept_stochastic_launch(const void* target, const void* draft, jt_dt
                                     float temperature, const float* u_accept,
                                     const float* u_sample, int32_t* accept_len,
                                     int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
-                                    hipStream_t stream) {
+                                    void* workspace, hipStream_t stream) {
+  double* ecache = static_cast<double*>(workspace);
   if (dt == JT_F32)
     hipLaunchKernelGGL(accept_stochastic_kernel<float>, dim3(batch), dim3(kStThreads), 0, stream,
                        static_cast<const float*>(target), static_cast<const float*>(draft),
                        max_nodes, vocab, depth_n, parent, token, depth, n_nodes, temperature,
-                       u_accept, u_sample, accept_len, accept_nodes, bonus_token, err);
+                       u_accept, u_sample, accept_len, accept_nodes, bonus_token, err, ecache);
   else
     hipLaunchKernelGGL(accept_stochastic_kernel<uint16_t>, dim3(batch), dim3(kStThreads), 0,
                        stream, static_cast<const uint16_t*>(target),
                        static_cast<const uint16_t*>(draft), max_nodes, vocab, depth_n, parent,
                        token, depth, n_nodes, temperature, u_accept, u_sample, accept_len,
-                       accept_nodes, bonus_token, err);
+                       accept_nodes, bonus_token, err, ecache);
   return hipGetLastError();
 }
 
