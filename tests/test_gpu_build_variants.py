@@ -126,3 +126,21 @@ def test_variant_reports_nan():
     L[0, 1, 3] = float("nan")
     g, err = _gpu_variant(L, 2, 4, [0], "node_block", 0.5)
     assert err & B.DERR_BAD_LOGIT
+
+
+@pytest.mark.parametrize("expand", ["candidate", "node_block"])
+def test_variant_max_budget(expand):
+    """B = 1023 (1024 nodes: every register slot of the search is used)."""
+    rng = np.random.default_rng(1023 if expand == "candidate" else 1024)
+    N, W, V, Bn = 12, 2, 64, 1023
+    L = torch.from_numpy((rng.standard_normal((2, N, V)) * 2).astype(np.float32))
+    roots = [5, 9]
+    for a in (0.0, 0.5):
+        g, err = _gpu_variant(L, W, Bn, roots, expand, a)
+        assert err == 0
+        for s in range(2):
+            t = O.build_tree_variant(L[s].numpy(), W, Bn, roots[s], expand, a)
+            assert t["n_nodes"] == 1024
+            if t["margin"] < _GAP or t["cross_ties"]:
+                continue
+            _check_seq(g, s, t)

@@ -469,3 +469,48 @@ def test_stochastic_rejects_bad_uniform():
     assert err & B.DERR_BAD_UNIFORM
     assert int(alen[1]) == 0 and int(bonus[1]) == -1
     assert int(bonus[0]) >= 0
+
+
+def test_stochastic_max_nodes():
+    """A 1024-node tree (the largest the call takes), correlated targets."""
+    rng = np.random.default_rng(4242)
+    b, T, V, N = 2, 1024, 48, 64
+    X, Dl, pars, deps, toks, ns = _correlated_case(rng, b, T, V, N, noise=0.4)
+    ns = [T, T]
+    pars, deps, toks = [], [], []
+    for s in range(b):
+        while True:
+            p, dd = _tree(rng, T)
+            if max(dd) <= N:
+                break
+        pars.append(p)
+        deps.append(dd)
+        tk = [0] + [int(rng.integers(0, V)) for _ in range(1, T)]
+        toks.append(tk)
+        for u in range(T):
+            if dd[u] < N:
+                X[s, u] = Dl[s, dd[u]] + 0.4 * rng.standard_normal(V)
+    ua = rng.random((b, T)).astype(np.float32)
+    us = rng.random(b).astype(np.float32)
+    Xt = torch.from_numpy(X.astype(np.float32))
+    Dt = torch.from_numpy(Dl.astype(np.float32))
+    alen, anodes, bonus, err = _gpu_stochastic(Xt, Dt, pars, toks, deps, ns, 1.0, ua, us)
+    assert err == 0
+    assert _compare_stochastic(Xt.numpy(), Dt.numpy(), pars, toks, deps, ns, N, 1.0, ua, us,
+                               alen, anodes, bonus) == b
+
+
+def test_margin_max_nodes():
+    rng = np.random.default_rng(77)
+    T, V, N = 1024, 32, 64
+    while True:
+        p, dd = _tree(rng, T)
+        if max(dd) <= N:
+            break
+    tok = [0] + [int(t) for t in rng.integers(0, V, T - 1)]
+    X = torch.from_numpy(np.round(rng.standard_normal((1, T, V)) * 2, 1).astype(np.float32))
+    alen, anodes, bonus, err = _gpu_margin(X, N, [p], [tok], [dd], [T], -1.0)
+    assert err == 0
+    L, nodes, bb = O.accept_margin(X[0].numpy(), p, tok, dd, T, N, -1.0)
+    assert (int(alen[0]), int(bonus[0])) == (L, bb)
+    assert np.array_equal(anodes[0], nodes)
