@@ -46,7 +46,7 @@ def _assert_tree_equal(g, ref, s, what):
 # ------------------------------------------------------------------ tree build
 
 BUILD_CASES = ([("tiny_f32", 0), ("qwen3_8b_b16", 0)] + [("qwen3_8b_b256", i) for i in range(8)]
-               + [("serving_b16", 0), ("qwen3_30b_a3b_b8", 0)])
+               + [("serving_b16", 0), ("serving_b32", 0), ("qwen3_30b_a3b_b8", 0)])
 
 
 @pytest.mark.parametrize("name,instance", BUILD_CASES)
@@ -279,6 +279,12 @@ def test_attention_serving_sampled(oracle_trees):
     _workload_attention("serving_b16", 0, oracle_trees, [], samp)
 
 
+def test_attention_serving_b32_sampled(oracle_trees):
+    """The batch-32 serving shape: sequences past the batch-16 ones."""
+    samp = [(s, [0, 2, 129, 256], [1, 16, 30]) for s in (16, 23, 31)]
+    _workload_attention("serving_b32", 0, oracle_trees, [], samp)
+
+
 def test_attention_long_prefix_sampled(oracle_trees):
     samp = [(s, [0, 3, 128, 255, 256], [0, 9, 31]) for s in (0, 7)]
     _workload_attention("qwen3_30b_a3b_b8", 0, oracle_trees, [], samp)
@@ -354,7 +360,8 @@ def test_accept_small_random_trees(seed):
 
 @pytest.mark.parametrize("name,instance,plant", [("tiny_f32", 0, True), ("qwen3_8b_b16", 0, False),
                                                  ("qwen3_8b_b256", 0, True),
-                                                 ("qwen3_8b_b256", 3, True)])
+                                                 ("qwen3_8b_b256", 3, True),
+                                                 ("serving_b32", 0, True)])
 def test_accept_workloads(name, instance, plant, oracle_trees):
     w = WL.WORKLOADS[name]
     _say(f"accept {name}#{instance}")
