@@ -36,7 +36,7 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default=WORKLOAD)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seqs", type=int, default=3,
+    ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences of the workload the CPU oracle is timed on")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device --steps times (a plain copy of known "
@@ -212,8 +212,26 @@ def main():
 
     def avg(a, b_):
         return sum(x_.elapsed_time(y_) for x_, y_ in zip(ev[a], ev[b_])) / len(ev[a])
+
+    def pct(a, b_):
+        v = np.sort([x_.elapsed_time(y_) for x_, y_ in zip(ev[a], ev[b_])])
+        return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+                "p90": float(np.percentile(v, 90))}
     stage_ms = {"build_tree": avg("s0", "s1"), "tree_meta": avg("s1", "s2"),
                 "tree_attention": avg("s2", "s3"), "accept": avg("s3", "s4")}
+    stage_pct = {"step": pct("s0", "s4"), "tree_attention": pct("s2", "s3")}
+
+    # the same step with the 256 MB last-level cache and L2 flushed before each
+    # step (an untimed 1 GiB write), timed step by step with events
+    flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    for k_ in ev:
+        ev[k_].clear()
+    for _ in range(args.steps):
+        flush.fill_(1)
+        step(True)
+    torch.cuda.synchronize()
+    flushed = {"step": pct("s0", "s4"), "tree_attention": pct("s2", "s3")}
+    del flush
     ms_step = wall * 1000.0 / args.steps
     n_nodes = tree["n_nodes"].cpu().numpy()
     depth = tree["depth"].cpu().numpy()
@@ -256,6 +274,8 @@ def main():
         "kv_gbps": kv_gbps,
         "kv_hbm_frac": kv_gbps / PEAK_HBM_GBPS,
         "stage_ms": stage_ms,
+        "stage_ms_pct": stage_pct,
+        "flushed_ms_pct": flushed,
         "accept_len": res[0].cpu().tolist(),
     }
     result["next_rows"] = time_next_rows(B, w, x, tree, d_draft, d_target, d_k, d_v, d_prefix,
