@@ -8,8 +8,8 @@
 // equals the target's choice.
 //
 // row_argmax: one workgroup per (vocab chunk, tree row, sequence) streams the
-//   target logits of rows < n_nodes once with 16-byte loads (HBM-bound) and
-//   keeps the best (value, lowest id).
+//   target logits of rows < n_nodes once with 16-byte non-temporal loads
+//   (HBM-bound; the rows are not reused) and keeps the best (value, lowest id).
 // accept_walk: one workgroup per sequence, one thread per node: merges the
 //   chunk winners, marks accepted nodes level by level (parent < child, so a
 //   level only reads the previous one) and picks the deepest accepted node.
@@ -24,6 +24,9 @@
 namespace jt {
 
 constexpr int kArgmaxThreads = 256;
+// 16-byte vectors for the streaming loads (read once: non-temporal)
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 constexpr int kWalkThreads = 1024;
 
 template <typename T, int VEC>
@@ -52,10 +55,10 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax(
         const int i = i0 + u * kArgmaxThreads * VEC;
         if (i < end) {
           if constexpr (sizeof(T) == 4) {
-            const float4 f = *reinterpret_cast<const float4*>(x + i);
+            const f32x4v f = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(x + i));
             v[u][0] = f.x; v[u][1] = f.y; v[u][2] = f.z; v[u][3] = f.w;
           } else {
-            const uint4 q = *reinterpret_cast<const uint4*>(x + i);
+            const u32x4v q = __builtin_nontemporal_load(reinterpret_cast<const u32x4v*>(x + i));
             const uint32_t w[4] = {q.x, q.y, q.z, q.w};
 #pragma unroll
             for (int k = 0; k < 4; ++k) {
