@@ -415,3 +415,19 @@ def test_build_tree_deep(N, W, Bb):
     for s in range(2):
         ref = O.build_tree(L[s], W, Bb, int(roots[s]), check_exact=False)
         _assert_tree_equal(g, ref, s, f"deep N={N}")
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_build_tree_ties_at_the_cut(seed):
+    """Integer-valued logits make many exact score ties, including at the B-th
+    score, where the selection's lower bound cuts the deeper levels."""
+    rng = np.random.default_rng(900 + seed)
+    N, W, V, b = 6, 4, 12, 3
+    L = rng.integers(-3, 3, (b, N, V)).astype(np.float32)
+    roots = rng.integers(0, V, b).astype(np.int32)
+    for Bb in (50, 123, 300):
+        g = _gpu_build(torch.from_numpy(L), W, Bb, torch.from_numpy(roots))
+        assert g["err"] == 0
+        for s in range(b):
+            ref = O.build_tree(L[s], W, Bb, int(roots[s]), check_exact=False)
+            _assert_tree_equal(g, ref, s, f"ties seed {seed} B={Bb}")

@@ -11,7 +11,10 @@
 //   level d-1 (a depth-d node in the final tree is preceded by its d-1
 //   ancestors, so no deeper position can be selected); the W candidate columns
 //   of a level are each sorted, so the level is their merge (merge path), and
-//   the sorted levels are merged the same way into the global pop order.  All
+//   the sorted levels are merged the same way into the global pop order.  Once
+//   B kept nodes score at or above some kept score, that score bounds the
+//   selection from below and later levels keep only children at or above it.
+//   All
 //   arithmetic on scores is fp64 and identical to a sequential evaluation
 //   except the per-depth log-sum-exp, whose summation order differs.
 // tree_select_seq (the variants): a literal best-first search, described below.
@@ -19,6 +22,7 @@
 #include "jt_host.h"
 
 #include <algorithm>
+#include <climits>
 #include <cmath>
 
 namespace jt {
@@ -252,20 +256,44 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   double* raw_cur = raw_b;
   int m_prev = 1;
   int last_level = 0;
+  // A lower bound tau of the B-th best score of the tree: any score t such
+  // that B kept nodes score >= t.  For the entries t of the newest level the
+  // count is (position + 1) plus, per earlier level, the entries >= t (binary
+  // search in its sorted list); tau is the largest entry whose count reaches
+  // B.  Children scoring below tau can never be selected, and since a
+  // column's scores fall with the parent position they form a suffix that is
+  // cut off.  The kept lists stay prefixes of the uncut ones, so the result
+  // is unchanged; deep levels usually empty out and the loop ends early.
+  __shared__ int s_istar;
+  double tau = -INFINITY;
+  int prev_cnt = 0;
   for (int d = 1; d <= depth_n; ++d) {
     const int cap = level_cap(d, width, budget);
     if (cap <= 0 || m_prev == 0) break;
     const double Sd = S[d];
-    // columns: list k holds children (p, k), p < len_k, at ms/mi[0] + k * cap
+    // column k holds children (p, k) of the first len_k parents
+    if (tid < L.wp) {
+      int lk = tid < width ? min(m_prev, cap / (tid + 1)) : 0;
+      if (tau != -INFINITY && lk > 0) {
+        const double c = static_cast<double>(cval[(d - 1) * WMAX + tid]);
+        int lo = 0, hi = lk;  // first parent whose child scores below tau
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if ((raw_prev[mid] + c) - Sd >= tau) lo = mid + 1; else hi = mid;
+        }
+        lk = lo;
+      }
+      lens[tid] = lk;
+    }
+    __syncthreads();
+    // columns: list k at ms/mi[0] + k * cap
     for (int idx = tid; idx < L.wp * cap; idx += kSelectThreads) {
       const int k = idx / cap, p = idx % cap;
-      const int len_k = k < width ? min(m_prev, cap / (k + 1)) : 0;
-      if (p < len_k) {
+      if (p < lens[k]) {
         ms[0][idx] = (raw_prev[p] + static_cast<double>(cval[(d - 1) * WMAX + k])) - Sd;
         mi[0][idx] = static_cast<uint32_t>(p) | (static_cast<uint32_t>(k) << 16);
       }
     }
-    if (tid < L.wp) lens[tid] = tid < width ? min(m_prev, cap / (tid + 1)) : 0;
     __syncthreads();
     int src = 0;
     for (int lists = L.wp; lists > 1; lists >>= 1) {
@@ -299,8 +327,30 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
       lv_info[loff[d] + o] = inf;
       raw_cur[o] = raw_prev[inf & 0xFFFFu] + static_cast<double>(cval[(d - 1) * WMAX + (inf >> 16)]);
     }
-    if (tid == 0) lcnt[d] = m_d;
+    if (tid == 0) {
+      lcnt[d] = m_d;
+      s_istar = INT_MAX;
+    }
     __syncthreads();
+    if (prev_cnt + m_d >= budget) {
+      for (int i = tid; i < m_d; i += kSelectThreads) {
+        const double t = lv_score[loff[d] + i];
+        int cnt = i + 1;
+        for (int dd = 1; dd < d; ++dd) {
+          const double* ls = lv_score + loff[dd];
+          int lo = 0, hi = lcnt[dd];  // entries >= t form a prefix
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (ls[mid] >= t) lo = mid + 1; else hi = mid;
+          }
+          cnt += lo;
+        }
+        if (cnt >= budget) atomicMin(&s_istar, i);
+      }
+      __syncthreads();
+      if (s_istar != INT_MAX) tau = fmax(tau, lv_score[loff[d] + s_istar]);
+    }
+    prev_cnt += m_d;
     double* t = raw_prev; raw_prev = raw_cur; raw_cur = t;
     m_prev = m_d;
     last_level = d;
