@@ -501,10 +501,15 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
     if (!(ph & 1)) issue((ph >> 1) + 2);
     const int j = ph - grp;  // this wave's step
     if (active && j >= 0 && j <= 2 * nt) {
-      if ((j & 1) == 0)
+      if ((j & 1) == 0) {
+        // the wave in its matrix step wins issue arbitration against the
+        // softmax of its partner on the SIMD (measured ~1% faster)
+        __builtin_amdgcn_s_setprio(1);
         matrix(j >> 1, nt);
-      else
+        __builtin_amdgcn_s_setprio(0);
+      } else {
         softmax((tb + (j >> 1)) * kKT);
+      }
     }
     if (ph & 1) {
       __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * IPW));
