@@ -144,7 +144,7 @@ def cpu_baseline(w, x, seqs):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1"}))
+        print(json.dumps({"error": "this benchmark runs on one GPU; the library has no multi-GPU path, so --gpus must be 1"}))
         sys.exit(2)
     if args.copy_probe > 0:
         copy_probe(args.copy_probe, args.steps)
