@@ -205,6 +205,10 @@ SMALL_ATTN = [
     (2, [31, 150], [20, 9], 20, 6, 3, 64, "f32"),
     (1, [64], [17], 17, 4, 1, 64, "f32"),
     (1, [513], [129], 129, 8, 8, 128, "f32"),
+    # one (sequence, KV head) group with a long prefix: both row tiles are
+    # split over more than 64 key ranges, the merge loops over lane chunks
+    (1, [20000], [40], 40, 8, 1, 128, "bf16"),
+    (1, [20000], [20], 20, 4, 1, 64, "bf16"),
 ]
 
 

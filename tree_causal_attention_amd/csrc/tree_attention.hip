@@ -55,6 +55,9 @@ constexpr int kAttnThreads = kWavesWG * kWave;
 constexpr int kStages = 4;           // K/V tile ring: a tile is fetched two pairs ahead
 constexpr int kMaxPagesLds = 4096;   // page ids staged per work item
 constexpr int kMaxTilesItem = kMaxPagesLds * kPage / kKT;
+// fewest key tiles per split of a row tile: shorter splits cost more in
+// per-workgroup set-up and partial rows than they gain in parallelism
+constexpr int kMinTilesSplit = 4;
 constexpr int kXcds = 8;             // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -565,15 +568,18 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   }
 }
 
-// Merges the per-split partials of the row tiles that were split.
+// Merges the per-split partials of the row tiles that were split: one wave
+// per row.  The split log-sum-exps are spread over the lanes (max and weight
+// sum by shuffles), then each lane accumulates its D / 64 output columns over
+// the splits with the loads of several splits in flight.
 template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine(AttnArgs a) {
-  constexpr int TPR = 64;  // threads per row
-  constexpr int PER = D / TPR;
+  constexpr int PER = D / kWave;  // output columns per lane
+  constexpr int kUnroll = 8;
   const int ctiles_full = a.s_full > 1 ? a.rt_full : 0;
   const int ctile = blockIdx.x / (kRowsWG / 4);
-  const int rloc = (blockIdx.x % (kRowsWG / 4)) * 4 + threadIdx.x / TPR;
-  const int t = threadIdx.x % TPR;
+  const int rloc = (blockIdx.x % (kRowsWG / 4)) * 4 + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
   const int sg = blockIdx.y, s = sg / a.hkv, g = sg % a.hkv;
   const int rt = ctile < ctiles_full ? ctile : a.rt_full;
   const int splits = rt < a.rt_full ? a.s_full : a.s_part;
@@ -583,29 +589,56 @@ __global__ __launch_bounds__(256) void tree_attn_combine(AttnArgs a) {
   const int r = rt * kRowsWG + rloc;
   if (r >= n * a.group) return;
   const int node = r / a.group, hq = g * a.group + r % a.group;
-  const size_t gbase = static_cast<size_t>(sg) * a.part_rows_group;
+  const size_t gbase = static_cast<size_t>(sg) * a.part_rows_group + rloc;
+  // partial row of split sp: gbase + sp0 + sp * kRowsWG
+  const int sp0 = part_row(a, rt, 0);
   float M = -INFINITY;
-  for (int sp = 0; sp < splits; ++sp)
-    M = fmaxf(M, a.part_lse[gbase + part_row(a, rt, sp) + rloc]);
+  for (int sp = lane; sp < splits; sp += kWave)
+    M = fmaxf(M, a.part_lse[gbase + sp0 + static_cast<size_t>(sp) * kRowsWG]);
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
   float acc[PER];
 #pragma unroll
   for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
   float wsum = 0.0f;
-  for (int sp = 0; sp < splits; ++sp) {
-    const size_t prow = gbase + part_row(a, rt, sp) + rloc;
-    const float ls = a.part_lse[prow];
-    if (ls == -INFINITY) continue;
-    const float wgt = expf(ls - M);
-    wsum += wgt;
+  for (int c0 = 0; c0 < splits; c0 += kWave) {
+    // this lane's split weight (0 for splits that saw no key of the row)
+    float wl = 0.0f;
+    if (c0 + lane < splits) {
+      const float ls = a.part_lse[gbase + sp0 + static_cast<size_t>(c0 + lane) * kRowsWG];
+      wl = (ls == -INFINITY) ? 0.0f : expf(ls - M);
+    }
+    wsum += wl;
+    const int cnt = min(kWave, splits - c0);
+    const float* po = a.part_o + (gbase + sp0 + static_cast<size_t>(c0) * kRowsWG) * D +
+                      lane * PER;
+    // kUnroll splits per round, all loads issued before the first use; slots
+    // past cnt reload the last split and get weight 0 (their lanes hold 0)
+    for (int k0 = 0; k0 < cnt; k0 += kUnroll) {
+      float v[kUnroll][PER];
 #pragma unroll
-    for (int k = 0; k < PER; ++k) acc[k] += wgt * a.part_o[prow * D + t + k * TPR];
+      for (int kk = 0; kk < kUnroll; ++kk) {
+        const int kc = min(k0 + kk, cnt - 1);
+#pragma unroll
+        for (int e = 0; e < PER; ++e) v[kk][e] = po[static_cast<size_t>(kc) * kRowsWG * D + e];
+      }
+#pragma unroll
+      for (int kk = 0; kk < kUnroll; ++kk) {
+        const float wk = __shfl(wl, k0 + kk, kWave);
+        // a zero weight contributes nothing, whatever the partial holds
+#pragma unroll
+        for (int e = 0; e < PER; ++e) acc[e] += (wk != 0.0f) ? wk * v[kk][e] : 0.0f;
+      }
+    }
   }
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) wsum += shfl_xor(wsum, m);
   const float inv = 1.0f / wsum;
   uint16_t* op = a.out + ((static_cast<size_t>(s) * a.max_nodes + node) * a.hq + hq) * D;
 #pragma unroll
   for (int k = 0; k < PER; ++k)
-    op[t + k * TPR] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[k] * inv));
-  if (a.lse && t == 0)
+    op[lane * PER + k] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[k] * inv));
+  if (a.lse && lane == 0)
     a.lse[(static_cast<size_t>(s) * a.max_nodes + node) * a.hq + hq] = M + logf(wsum);
 }
 
@@ -700,11 +733,12 @@ static AttnPlan attn_plan(const AttnShape& s) {
   const long long full_items = static_cast<long long>(p.ngroups) * p.rt_full;
   int sf = full_items > 0 ? static_cast<int>((256 + full_items - 1) / full_items) : 1;
   if (full_items >= 192) sf = 1;
-  p.s_full = std::max(min_splits, std::min(sf, std::max(1, tiles)));
+  const int max_splits = std::max(1, tiles / kMinTilesSplit);
+  p.s_full = std::max(min_splits, std::min(sf, max_splits));
   // the partial tile has few rows: split it finely so it trails the full tiles
   int sp = static_cast<int>((256 + p.ngroups - 1) / std::max(1, p.ngroups));
   sp = std::max(sp, 4);
-  p.s_part = p.has_partial ? std::max(min_splits, std::min(sp, std::max(1, tiles))) : 0;
+  p.s_part = p.has_partial ? std::max(min_splits, std::min(sp, max_splits)) : 0;
   const int items = p.rt_full * p.s_full + p.has_partial * p.s_part;
   const int gx_max = (p.ngroups + kXcds - 1) / kXcds;
   p.slots_per_xcd = gx_max * items;
