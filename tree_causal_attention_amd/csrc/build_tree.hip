@@ -333,20 +333,26 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
     }
     __syncthreads();
     if (prev_cnt + m_d >= budget) {
-      for (int i = tid; i < m_d; i += kSelectThreads) {
+      // count[i] = i + 1 + sum over earlier levels of their entries >= the
+      // i-th entry; one (entry, earlier level) binary search per thread step,
+      // summed by LDS atomics (the merge buffers are free until the next level)
+      int* cnt = reinterpret_cast<int*>(mi[0]);
+      for (int i = tid; i < m_d; i += kSelectThreads) cnt[i] = i + 1;
+      __syncthreads();
+      for (int x = tid; x < m_d * (d - 1); x += kSelectThreads) {
+        const int i = x % m_d, dd = 1 + x / m_d;
         const double t = lv_score[loff[d] + i];
-        int cnt = i + 1;
-        for (int dd = 1; dd < d; ++dd) {
-          const double* ls = lv_score + loff[dd];
-          int lo = 0, hi = lcnt[dd];  // entries >= t form a prefix
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (ls[mid] >= t) lo = mid + 1; else hi = mid;
-          }
-          cnt += lo;
+        const double* ls = lv_score + loff[dd];
+        int lo = 0, hi = lcnt[dd];  // entries >= t form a prefix
+        while (lo < hi) {
+          const int mid = (lo + hi) >> 1;
+          if (ls[mid] >= t) lo = mid + 1; else hi = mid;
         }
-        if (cnt >= budget) atomicMin(&s_istar, i);
+        if (lo > 0) atomicAdd(&cnt[i], lo);
       }
+      __syncthreads();
+      for (int i = tid; i < m_d; i += kSelectThreads)
+        if (cnt[i] >= budget) atomicMin(&s_istar, i);
       __syncthreads();
       if (s_istar != INT_MAX) tau = fmax(tau, lv_score[loff[d] + s_istar]);
     }
