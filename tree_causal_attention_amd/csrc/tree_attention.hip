@@ -576,9 +576,13 @@ template <int D>
 __global__ __launch_bounds__(256) void tree_attn_combine(AttnArgs a) {
   constexpr int PER = D / kWave;  // output columns per lane
   constexpr int kUnroll = 8;
+  // blocks of 4 rows: kRowsWG / 4 per split full row tile, then enough for
+  // the rows of the split last row tile
   const int ctiles_full = a.s_full > 1 ? a.rt_full : 0;
-  const int ctile = blockIdx.x / (kRowsWG / 4);
-  const int rloc = (blockIdx.x % (kRowsWG / 4)) * 4 + threadIdx.x / kWave;
+  const int bfull = ctiles_full * (kRowsWG / 4);
+  const int ctile = blockIdx.x < bfull ? blockIdx.x / (kRowsWG / 4) : ctiles_full;
+  const int rloc = (blockIdx.x < bfull ? blockIdx.x % (kRowsWG / 4) : blockIdx.x - bfull) * 4 +
+                   threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
   const int sg = blockIdx.y, s = sg / a.hkv, g = sg % a.hkv;
   const int rt = ctile < ctiles_full ? ctile : a.rt_full;
@@ -715,7 +719,7 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32(
 // ------------------------------------------------------------------ host side
 
 struct AttnPlan {
-  int rt_full, has_partial, s_full, s_part, ngroups, slots_per_xcd, ctiles;
+  int rt_full, has_partial, s_full, s_part, ngroups, slots_per_xcd, cblocks;
   int part_rows_group, full_part_rows;
   size_t off_lse, bytes;
 };
@@ -744,10 +748,13 @@ static AttnPlan attn_plan(const AttnShape& s) {
   p.slots_per_xcd = gx_max * items;
   p.full_part_rows = p.s_full > 1 ? p.rt_full * p.s_full * kRowsWG : 0;
   p.part_rows_group = p.full_part_rows + ((p.has_partial && p.s_part > 1) ? p.s_part * kRowsWG : 0);
-  p.ctiles = (p.s_full > 1 ? p.rt_full : 0) + ((p.has_partial && p.s_part > 1) ? 1 : 0);
+  // merge blocks (4 rows each): the split full row tiles, then the rows of a
+  // split last row tile
+  p.cblocks = (p.s_full > 1 ? p.rt_full * (kRowsWG / 4) : 0) +
+              ((p.has_partial && p.s_part > 1) ? (rmax - p.rt_full * kRowsWG + 3) / 4 : 0);
   if (s.dt == JT_F32) {
     p.part_rows_group = 0;
-    p.ctiles = 0;
+    p.cblocks = 0;
   }
   if (p.part_rows_group > 0) {
     const size_t rows = static_cast<size_t>(p.ngroups) * p.part_rows_group;
@@ -768,8 +775,8 @@ static hipError_t launch_mfma(const AttnShape& sh, const AttnPlan& p, AttnArgs& 
   hipLaunchKernelGGL(tree_attn_mfma<D>, dim3(kXcds * p.slots_per_xcd), dim3(kAttnThreads), 0,
                      stream, a);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess || p.ctiles == 0) return e;
-  hipLaunchKernelGGL(tree_attn_combine<D>, dim3(p.ctiles * (kRowsWG / 4), p.ngroups), dim3(256),
+  if (e != hipSuccess || p.cblocks == 0) return e;
+  hipLaunchKernelGGL(tree_attn_combine<D>, dim3(p.cblocks, p.ngroups), dim3(256),
                      0, stream, a);
   return hipGetLastError();
 }
