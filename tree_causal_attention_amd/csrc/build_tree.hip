@@ -567,20 +567,21 @@ __global__ __launch_bounds__(kSeqThreads) void tree_select_seq(
       const int du = dep[u];
       const int c = min(width, budget - (n - 1));
       if (tid == u % kSeqThreads) qi[u / kSeqThreads] = -1;
-      for (int k = 0; k < c; ++k) {
+      // child k is node v = n + k, owned by thread v % kSeqThreads: the c <= W
+      // children land on distinct threads and are attached together
+      const int k = (tid - n % kSeqThreads + kSeqThreads) % kSeqThreads;
+      if (k < c) {
         const int v = n + k;
-        if (tid == v % kSeqThreads) {
-          const int s = v / kSeqThreads;
-          const double rv = raw[u] + static_cast<double>(cval[du * WMAX + k]);
-          const double sc = rv - S[du + 1];
-          raw[v] = rv;
-          dep[v] = du + 1;
-          parent[base + v] = u;
-          token[base + v] = ctok[du * WMAX + k];
-          depth[base + v] = du + 1;
-          if (score_out) score_out[base + v] = sc;
-          if (du + 1 < depth_n) { qi[s] = v; qk[s] = variant_key(sc, ent[du], a); }
-        }
+        const int s = v / kSeqThreads;
+        const double rv = raw[u] + static_cast<double>(cval[du * WMAX + k]);
+        const double sc = rv - S[du + 1];
+        raw[v] = rv;
+        dep[v] = du + 1;
+        parent[base + v] = u;
+        token[base + v] = ctok[du * WMAX + k];
+        depth[base + v] = du + 1;
+        if (score_out) score_out[base + v] = sc;
+        if (du + 1 < depth_n) { qi[s] = v; qk[s] = variant_key(sc, ent[du], a); }
       }
       n += c;
     }
