@@ -59,6 +59,8 @@ constexpr int kMaxTilesItem = kMaxPagesLds * kPage / kKT;
 // per-workgroup set-up and partial rows than they gain in parallelism
 constexpr int kMinTilesSplit = 4;
 constexpr int kXcds = 8;             // MI355X: 8 XCDs, workgroups dealt round-robin
+constexpr double kCusPerXcd = 32.0;  // 256 CUs
+constexpr double kPartialTileCost = 0.625;  // partial-tile / full-tile time per key tile
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kRescaleThreshold = 8.0f;
@@ -743,6 +745,20 @@ static AttnPlan attn_plan(const AttnShape& s) {
   int sp = static_cast<int>((256 + p.ngroups - 1) / std::max(1, p.ngroups));
   sp = std::max(sp, 4);
   p.s_part = p.has_partial ? std::max(min_splits, std::min(sp, max_splits)) : 0;
+  // Few full row tiles (one or two sequences): rather than a second wave of
+  // workgroups for the partial tile, fit every split of both kinds into one
+  // wave of the XCD's CUs.  A partial-tile workgroup (one active wave) streams
+  // a key tile in about 5/8 of a full one's time, so it gets 5/8 as many
+  // splits for the same finishing time.
+  if (full_items > 0 && full_items < 192 && p.has_partial) {
+    const int gx = (p.ngroups + kXcds - 1) / kXcds;
+    const int sf1 = static_cast<int>(kCusPerXcd / (gx * (p.rt_full + kPartialTileCost)));
+    if (sf1 >= 2) {
+      const int sp1 = std::max(1, static_cast<int>(kPartialTileCost * sf1 + 0.5));
+      p.s_full = std::max(min_splits, std::min(sf1, max_splits));
+      p.s_part = std::max(min_splits, std::min(sp1, max_splits));
+    }
+  }
   const int items = p.rt_full * p.s_full + p.has_partial * p.s_part;
   const int gx_max = (p.ngroups + kXcds - 1) / kXcds;
   p.slots_per_xcd = gx_max * items;
