@@ -209,6 +209,11 @@ SMALL_ATTN = [
     # split over more than 64 key ranges, the merge loops over lane chunks
     (1, [20000], [40], 40, 8, 1, 128, "bf16"),
     (1, [20000], [20], 20, 4, 1, 64, "bf16"),
+    # the largest trees the call takes (1024 nodes, 32 mask words) with the
+    # largest GQA group (16): 64 full row tiles per (sequence, KV head)
+    (1, [100], [1024], 1024, 16, 1, 128, "bf16"),
+    (2, [0, 37], [1024, 999], 1024, 16, 1, 64, "bf16"),
+    (1, [10], [1024], 1024, 16, 1, 64, "f32"),
 ]
 
 
