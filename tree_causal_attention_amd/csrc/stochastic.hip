@@ -28,6 +28,9 @@ namespace jt {
 
 constexpr int kStThreads = 1024;
 constexpr int kStWaves = kStThreads / kWave;
+// Passes over the vocabulary load kStUnroll entries per thread before using
+// them: one workgroup streams a whole row, so its loads in flight set the pace.
+constexpr int kStUnroll = 8;
 
 template <typename T>
 struct RowView {
@@ -78,19 +81,39 @@ __device__ void row_stats(RowView<T> r, int vocab, double tinv, float* m_out, do
                           int* redi) {
   float m = -INFINITY;
   int b = 0;
-  for (int i = threadIdx.x; i < vocab; i += kStThreads) {
-    const float x = r.at(i);
-    if (x != x || x == INFINITY) b = 1;
-    m = fmaxf(m, x);
+  for (int i0 = threadIdx.x; i0 < vocab; i0 += kStThreads * kStUnroll) {
+    float x[kStUnroll];
+#pragma unroll
+    for (int k = 0; k < kStUnroll; ++k) {
+      const int i = i0 + k * kStThreads;
+      x[k] = i < vocab ? r.at(i) : -INFINITY;
+    }
+#pragma unroll
+    for (int k = 0; k < kStUnroll; ++k) {
+      if (x[k] != x[k] || x[k] == INFINITY) b = 1;
+      m = fmaxf(m, x[k]);
+    }
   }
   m = block_max(m, redf);
   b = block_or(b, redi);
   double z = 0.0;
   if (!b && m != -INFINITY)
-    for (int i = threadIdx.x; i < vocab; i += kStThreads) {
-      const double e = exp((static_cast<double>(r.at(i)) - static_cast<double>(m)) * tinv);
-      e_out[i] = e;
-      z += e;
+    for (int i0 = threadIdx.x; i0 < vocab; i0 += kStThreads * kStUnroll) {
+      float x[kStUnroll];
+#pragma unroll
+      for (int k = 0; k < kStUnroll; ++k) {
+        const int i = i0 + k * kStThreads;
+        x[k] = i < vocab ? r.at(i) : m;
+      }
+#pragma unroll
+      for (int k = 0; k < kStUnroll; ++k) {
+        const int i = i0 + k * kStThreads;
+        if (i < vocab) {
+          const double e = exp((static_cast<double>(x[k]) - static_cast<double>(m)) * tinv);
+          e_out[i] = e;
+          z += e;
+        }
+      }
     }
   z = block_sum(z, redd);  // its barriers also publish e_out to the workgroup
   *m_out = m;
@@ -190,7 +213,17 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
       // rejection: c' = c + U / zd, U' = sum_y max(0, et - c' ed)
       const double c_new = c + U / zd;
       double part = 0.0;
-      for (int i = tid; i < vocab; i += kStThreads) part += fmax(0.0, et[i] - c_new * ed[i]);
+      for (int i0 = tid; i0 < vocab; i0 += kStThreads * kStUnroll) {
+        double a[kStUnroll], q[kStUnroll];
+#pragma unroll
+        for (int k = 0; k < kStUnroll; ++k) {
+          const int i = i0 + k * kStThreads;
+          a[k] = i < vocab ? et[i] : 0.0;
+          q[k] = i < vocab ? ed[i] : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < kStUnroll; ++k) part += fmax(0.0, a[k] - c_new * q[k]);
+      }
       const double un = block_sum(part, redd);
       if (un == 0.0) break;  // no mass left: keep the previous distribution
       c = c_new;
@@ -210,7 +243,16 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
   const int seg = (vocab + kStWaves * kWave - 1) / (kStWaves * kWave) * kWave;
   const int s0 = min(vocab, wv * seg), s1 = min(vocab, s0 + seg);
   double own = 0.0;
-  for (int i = s0 + lane; i < s1; i += kWave) own += weight(i);
+  for (int i0 = s0 + lane; i0 < s1; i0 += kWave * kStUnroll) {
+    double w[kStUnroll];
+#pragma unroll
+    for (int k = 0; k < kStUnroll; ++k) {
+      const int i = i0 + k * kWave;
+      w[k] = i < s1 ? weight(i) : 0.0;
+    }
+#pragma unroll
+    for (int k = 0; k < kStUnroll; ++k) own += w[k];
+  }
   for (int o = 32; o > 0; o >>= 1) own += __shfl_xor(own, o, kWave);
   if (lane == 0) wsum[wv] = own;
   __syncthreads();
@@ -230,19 +272,30 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
   if (s0 < s1 && wpre[wv] <= thr && wpre[wv] + wsum[wv] > thr) {
     double carry = wpre[wv];
     int y = -1, last_pos = -1;
-    for (int r0 = s0; r0 < s1 && y < 0; r0 += kWave) {
-      const int i = r0 + lane;
-      const double w = i < s1 ? weight(i) : 0.0;
-      double incl = w;  // inclusive prefix over the 64 lanes
-      for (int o = 1; o < kWave; o <<= 1) {
-        const double up = __shfl_up(incl, o, kWave);
-        if (lane >= o) incl += up;
+    // 64-entry chunks in order, kStUnroll chunks loaded at a time
+    for (int b0 = s0; b0 < s1 && y < 0; b0 += kWave * kStUnroll) {
+      double wk[kStUnroll];
+#pragma unroll
+      for (int k = 0; k < kStUnroll; ++k) {
+        const int i = b0 + k * kWave + lane;
+        wk[k] = i < s1 ? weight(i) : 0.0;
       }
-      const unsigned long long hit = __ballot(carry + incl > thr);
-      const unsigned long long pos = __ballot(w > 0.0);
-      if (pos) last_pos = r0 + 63 - __clzll(pos);
-      if (hit) y = r0 + __ffsll(static_cast<long long>(hit)) - 1;
-      carry += __shfl(incl, kWave - 1, kWave);
+#pragma unroll
+      for (int k = 0; k < kStUnroll; ++k) {
+        const int r0 = b0 + k * kWave;
+        if (y >= 0 || r0 >= s1) break;  // wave-uniform
+        const double w = wk[k];
+        double incl = w;  // inclusive prefix over the 64 lanes
+        for (int o = 1; o < kWave; o <<= 1) {
+          const double up = __shfl_up(incl, o, kWave);
+          if (lane >= o) incl += up;
+        }
+        const unsigned long long hit = __ballot(carry + incl > thr);
+        const unsigned long long pos = __ballot(w > 0.0);
+        if (pos) last_pos = r0 + 63 - __clzll(pos);
+        if (hit) y = r0 + __ffsll(static_cast<long long>(hit)) - 1;
+        carry += __shfl(incl, kWave - 1, kWave);
+      }
     }
     if (lane == 0) pick = y >= 0 ? y : last_pos;  // re-summation rounding: last positive weight
   }
