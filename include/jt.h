@@ -369,9 +369,12 @@ jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int n
  *             are then zero / -1).
  *   workspace  jt_accept_stochastic_workspace(batch, vocab) bytes (2 * vocab
  *             doubles per sequence: the exponentials of the current target
- *             row and of the children's draft row, reused by every pass).
+ *             row and of the children's draft row, reused by every pass; then
+ *             16 bytes per 4096-entry chunk of the root's target row and the
+ *             depth-1 draft row, whose statistics are computed up front).
  * Limits: batch >= 0, 1 <= max_nodes <= 1024, vocab >= 1, 1 <= depth_n <= 64.
- * One workgroup per sequence.
+ * Two short pre-pass kernels over every sequence's first two rows, then one
+ * workgroup per sequence for the walk.
  * ---------------------------------------------------------------------- */
 size_t jt_accept_stochastic_workspace(int batch, int vocab);
 jt_status jt_accept_stochastic(const void* target_logits, const void* draft_logits, jt_dtype dt,

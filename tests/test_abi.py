@@ -158,7 +158,9 @@ def test_accept_stochastic_validation(lib):
     p = ctypes.c_void_p(1)
 
     need = lib.jt_accept_stochastic_workspace(1, 100)
-    assert need == 2 * 100 * 8
+    # 2 x 100 doubles (et, ed) padded to 256 bytes, then one 4096-entry chunk
+    # for each of the two pre-pass rows: sum (8) + max (4) + flag (4) bytes
+    assert need == 1792 + 2 * 16
 
     def call(temp=0.7, dt=1, b=1, T=17, V=100, N=4, ua=p, ws=need):
         return f(p, p, dt, b, T, V, N, p, p, p, p, temp, ua, p, p, p, p, None, p, ws, None)

@@ -21,6 +21,11 @@
 // multiply-add per entry.  When no child is accepted the bonus token is the
 // inverse-CDF draw of u_sample over the residual weights.  All probability
 // arithmetic is fp64 (exp from the device math library).
+//
+// Every walk starts at the root with the depth-1 draft row, so the statistics
+// of those two rows are computed beforehand across the whole GPU (chunk
+// maxima, then the exponentials and per-chunk fp64 sums); the walk adds the
+// chunk sums in chunk order and computes deeper rows itself.
 #include "jt_device.h"
 #include "jt_host.h"
 
@@ -31,6 +36,115 @@ constexpr int kStWaves = kStThreads / kWave;
 // Passes over the vocabulary load kStUnroll entries per thread before using
 // them: one workgroup streams a whole row, so its loads in flight set the pace.
 constexpr int kStUnroll = 8;
+constexpr int kPreThreads = 256;
+constexpr int kPreChunk = kPreThreads * 16;  // entries of one pre-pass workgroup
+
+// Workspace: et and ed (2 * vocab doubles per sequence), then per sequence
+// and pre-pass row (0: the root's target row, 1: the depth-1 draft row) the
+// chunk sums (double), maxima (float) and bad flags (int).
+struct StWorkspace {
+  size_t off_sum, off_max, off_bad, bytes;
+  int nch;
+};
+
+static __host__ __device__ StWorkspace st_workspace(int batch, int vocab) {
+  StWorkspace w{};
+  w.nch = (vocab + kPreChunk - 1) / kPreChunk;
+  const size_t cells = static_cast<size_t>(batch) * 2 * w.nch;
+  w.off_sum = (static_cast<size_t>(batch) * 2 * vocab * sizeof(double) + 255) / 256 * 256;
+  w.off_max = w.off_sum + cells * sizeof(double);
+  w.off_bad = w.off_max + cells * sizeof(float);
+  w.bytes = w.off_bad + cells * sizeof(int);
+  return w;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* pre_row(const T* target, const T* draft, int seq, int r,
+                                            int max_nodes, int depth_n, int vocab) {
+  return r == 0 ? target + static_cast<size_t>(seq) * max_nodes * vocab
+                : draft + static_cast<size_t>(seq) * depth_n * vocab;
+}
+
+// Pre-pass 1: maximum and NaN / +inf flag of each chunk of the two rows.
+template <typename T>
+__global__ __launch_bounds__(kPreThreads) void stoch_pre_max(
+    const T* __restrict__ target, const T* __restrict__ draft, int max_nodes, int vocab,
+    int depth_n, int nch, float* __restrict__ cmax, int* __restrict__ cbad) {
+  __shared__ float rm[kPreThreads / kWave];
+  __shared__ int rb[kPreThreads / kWave];
+  // workgroup = (chunk, row, sequence), chunk fastest
+  const int c = blockIdx.x % nch, r = (blockIdx.x / nch) % 2, seq = blockIdx.x / nch / 2;
+  const T* row = pre_row(target, draft, seq, r, max_nodes, depth_n, vocab);
+  float m = -INFINITY;
+  int b = 0;
+  float x[kPreChunk / kPreThreads];
+#pragma unroll
+  for (int k = 0; k < kPreChunk / kPreThreads; ++k) {
+    const int i = c * kPreChunk + k * kPreThreads + threadIdx.x;
+    x[k] = i < vocab ? load_as_f32(row, i) : -INFINITY;
+  }
+#pragma unroll
+  for (int k = 0; k < kPreChunk / kPreThreads; ++k) {
+    if (x[k] != x[k] || x[k] == INFINITY) b = 1;
+    m = fmaxf(m, x[k]);
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    m = fmaxf(m, __shfl_xor(m, o, kWave));
+    b |= __shfl_xor(b, o, kWave);
+  }
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  if (lane == 0) { rm[wv] = m; rb[wv] = b; }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kPreThreads / kWave; ++k) { m = fmaxf(m, rm[k]); b |= rb[k]; }
+    const size_t cell = (static_cast<size_t>(seq) * 2 + r) * nch + c;
+    cmax[cell] = m;
+    cbad[cell] = b;
+  }
+}
+
+// Pre-pass 2: row maximum from the chunk maxima, then exp((x - max) / T) into
+// et (r = 0) or ed (r = 1) and the chunk's fp64 sum (fixed summation order).
+template <typename T>
+__global__ __launch_bounds__(kPreThreads) void stoch_pre_exp(
+    const T* __restrict__ target, const T* __restrict__ draft, int max_nodes, int vocab,
+    int depth_n, int nch, double tinv, const float* __restrict__ cmax,
+    const int* __restrict__ cbad, double* __restrict__ csum, double* __restrict__ ecache) {
+  __shared__ double rs[kPreThreads / kWave];
+  const int c = blockIdx.x % nch, r = (blockIdx.x / nch) % 2, seq = blockIdx.x / nch / 2;
+  const size_t cell0 = (static_cast<size_t>(seq) * 2 + r) * nch;
+  float m = -INFINITY;
+  int b = 0;
+  for (int k = 0; k < nch; ++k) { m = fmaxf(m, cmax[cell0 + k]); b |= cbad[cell0 + k]; }
+  double z = 0.0;
+  if (!b && m != -INFINITY) {
+    const T* row = pre_row(target, draft, seq, r, max_nodes, depth_n, vocab);
+    double* e_out = ecache + (static_cast<size_t>(seq) * 2 + r) * vocab;
+    float x[kPreChunk / kPreThreads];
+#pragma unroll
+    for (int k = 0; k < kPreChunk / kPreThreads; ++k) {
+      const int i = c * kPreChunk + k * kPreThreads + threadIdx.x;
+      x[k] = i < vocab ? load_as_f32(row, i) : m;
+    }
+#pragma unroll
+    for (int k = 0; k < kPreChunk / kPreThreads; ++k) {
+      const int i = c * kPreChunk + k * kPreThreads + threadIdx.x;
+      if (i < vocab) {
+        const double e = exp((static_cast<double>(x[k]) - static_cast<double>(m)) * tinv);
+        e_out[i] = e;
+        z += e;
+      }
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, kWave);
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  if (lane == 0) rs[wv] = z;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    for (int k = 1; k < kPreThreads / kWave; ++k) z += rs[k];
+    csum[cell0 + c] = z;
+  }
+}
 
 template <typename T>
 struct RowView {
@@ -128,7 +242,9 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
     const int32_t* __restrict__ depth, const int32_t* __restrict__ n_nodes, float temperature,
     const float* __restrict__ u_accept, const float* __restrict__ u_sample,
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
-    int32_t* __restrict__ bonus_token, int32_t* err, double* __restrict__ ecache) {
+    int32_t* __restrict__ bonus_token, int32_t* err, double* __restrict__ ecache,
+    const double* __restrict__ pre_sum, const float* __restrict__ pre_max,
+    const int* __restrict__ pre_bad, int nch) {
   __shared__ int par[1024];
   __shared__ float redf[kStWaves];
   __shared__ double redd[kStWaves];
@@ -179,6 +295,22 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
   if (b) { fail(b); return; }
 
   const double tinv = 1.0 / static_cast<double>(temperature);
+  // statistics of pre-pass row r (0: root target row, 1: depth-1 draft row),
+  // whose exponentials are already in et / ed; chunk sums added in order
+  auto pre_stats = [&](int r, float* m_out, double* z_out, bool* bad) {
+    const size_t cell0 = (static_cast<size_t>(seq) * 2 + r) * nch;
+    float m = -INFINITY;
+    int bb = 0;
+    double z = 0.0;
+    for (int k = 0; k < nch; ++k) {
+      m = fmaxf(m, pre_max[cell0 + k]);
+      bb |= pre_bad[cell0 + k];
+      z += pre_sum[cell0 + k];
+    }
+    *m_out = m;
+    *z_out = z;
+    *bad = bb || m == -INFINITY;
+  };
   const T* draft_seq = draft + static_cast<size_t>(seq) * depth_n * vocab;
   int u = 0, L = 0;
   // current distribution: weights max(0, et - c ed) over the current node's
@@ -187,8 +319,11 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
   double zt = 1.0, zd = 1.0, c = 0.0, U = 1.0;
   while (true) {
     bool bad = false;
-    row_stats(RowView<T>{target + (base + u) * vocab}, vocab, tinv, &mt, &zt, &bad, et, redf,
-              redd, redi);
+    if (u == 0)
+      pre_stats(0, &mt, &zt, &bad);
+    else
+      row_stats(RowView<T>{target + (base + u) * vocab}, vocab, tinv, &mt, &zt, &bad, et, redf,
+                redd, redi);
     if (bad) { fail(JT_DERR_BAD_LOGIT); return; }
     c = 0.0;
     U = zt;
@@ -198,8 +333,11 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
       if (par[v] != u) continue;  // uniform: par is in LDS, v is uniform
       if (!have_q) {
         const int d = depth[base + v];
-        row_stats(RowView<T>{draft_seq + static_cast<size_t>(d - 1) * vocab}, vocab, tinv, &md,
-                  &zd, &bad, ed, redf, redd, redi);
+        if (d == 1)
+          pre_stats(1, &md, &zd, &bad);
+        else
+          row_stats(RowView<T>{draft_seq + static_cast<size_t>(d - 1) * vocab}, vocab, tinv, &md,
+                    &zd, &bad, ed, redf, redd, redi);
         if (bad) { fail(JT_DERR_BAD_LOGIT); return; }
         have_q = true;
       }
@@ -308,7 +446,7 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
 }
 
 size_t accept_stochastic_workspace_bytes(int batch, int vocab) {
-  return static_cast<size_t>(batch) * 2 * vocab * sizeof(double);
+  return st_workspace(batch, vocab).bytes;
 }
 
 hipError_t accept_stochastic_launch(const void* target, const void* draft, jt_dtype dt,
@@ -319,18 +457,32 @@ hipError_t accept_stochastic_launch(const void* target, const void* draft, jt_dt
                                     const float* u_sample, int32_t* accept_len,
                                     int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
                                     void* workspace, hipStream_t stream) {
-  double* ecache = static_cast<double*>(workspace);
+  unsigned char* ws = static_cast<unsigned char*>(workspace);
+  double* ecache = reinterpret_cast<double*>(ws);
+  const StWorkspace L = st_workspace(batch, vocab);
+  double* csum = reinterpret_cast<double*>(ws + L.off_sum);
+  float* cmax = reinterpret_cast<float*>(ws + L.off_max);
+  int* cbad = reinterpret_cast<int*>(ws + L.off_bad);
+  const double tinv = 1.0 / static_cast<double>(temperature);
+  const dim3 pre_grid(static_cast<unsigned>(L.nch) * 2u * static_cast<unsigned>(batch));
+#define JT_ST_LAUNCH(TT)                                                                        \
+  do {                                                                                          \
+    const TT* tg = static_cast<const TT*>(target);                                              \
+    const TT* dr = static_cast<const TT*>(draft);                                               \
+    hipLaunchKernelGGL(stoch_pre_max<TT>, pre_grid, dim3(kPreThreads), 0, stream, tg, dr,       \
+                       max_nodes, vocab, depth_n, L.nch, cmax, cbad);                           \
+    hipLaunchKernelGGL(stoch_pre_exp<TT>, pre_grid, dim3(kPreThreads), 0, stream, tg, dr,       \
+                       max_nodes, vocab, depth_n, L.nch, tinv, cmax, cbad, csum, ecache);       \
+    hipLaunchKernelGGL(accept_stochastic_kernel<TT>, dim3(batch), dim3(kStThreads), 0, stream,  \
+                       tg, dr, max_nodes, vocab, depth_n, parent, token, depth, n_nodes,        \
+                       temperature, u_accept, u_sample, accept_len, accept_nodes, bonus_token,  \
+                       err, ecache, csum, cmax, cbad, L.nch);                                   \
+  } while (0)
   if (dt == JT_F32)
-    hipLaunchKernelGGL(accept_stochastic_kernel<float>, dim3(batch), dim3(kStThreads), 0, stream,
-                       static_cast<const float*>(target), static_cast<const float*>(draft),
-                       max_nodes, vocab, depth_n, parent, token, depth, n_nodes, temperature,
-                       u_accept, u_sample, accept_len, accept_nodes, bonus_token, err, ecache);
+    JT_ST_LAUNCH(float);
   else
-    hipLaunchKernelGGL(accept_stochastic_kernel<uint16_t>, dim3(batch), dim3(kStThreads), 0,
-                       stream, static_cast<const uint16_t*>(target),
-                       static_cast<const uint16_t*>(draft), max_nodes, vocab, depth_n, parent,
-                       token, depth, n_nodes, temperature, u_accept, u_sample, accept_len,
-                       accept_nodes, bonus_token, err, ecache);
+    JT_ST_LAUNCH(uint16_t);
+#undef JT_ST_LAUNCH
   return hipGetLastError();
 }
 
