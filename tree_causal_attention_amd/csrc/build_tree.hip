@@ -472,6 +472,32 @@ __device__ __forceinline__ bool seq_better(double ka, int ia, double kb, int ib)
   return ka > kb || (ka == kb && ia < ib);
 }
 
+// One step of a wave argmax over (key, id) through a DPP lane move: take the
+// other lane's pair when it is better.  Lanes the move does not reach (row
+// mask) keep their own pair.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_best(double& k, int& id) {
+  const uint2 kb = __builtin_bit_cast(uint2, k);
+  uint2 ob;
+  ob.x = __builtin_amdgcn_update_dpp(kb.x, kb.x, CTRL, ROW_MASK, 0xF, false);
+  ob.y = __builtin_amdgcn_update_dpp(kb.y, kb.y, CTRL, ROW_MASK, 0xF, false);
+  const int oi = __builtin_amdgcn_update_dpp(id, id, CTRL, ROW_MASK, 0xF, false);
+  const double ok = __builtin_bit_cast(double, ob);
+  if (seq_better(ok, oi, k, id)) { k = ok; id = oi; }
+}
+
+// Wave argmax of (key, id) into lane 63: quad swaps, rotations by 4 and 8
+// inside each row of 16 lanes, then row broadcasts 15 and 31 (the order is
+// total, so any combination order gives the same winner).
+__device__ __forceinline__ void wave_best_to_lane63(double& k, int& id) {
+  dpp_best<0xB1, 0xF>(k, id);   // quad_perm [1, 0, 3, 2]
+  dpp_best<0x4E, 0xF>(k, id);   // quad_perm [2, 3, 0, 1]
+  dpp_best<0x124, 0xF>(k, id);  // row_ror 4
+  dpp_best<0x128, 0xF>(k, id);  // row_ror 8
+  dpp_best<0x142, 0xA>(k, id);  // row_bcast 15 into rows 1 and 3
+  dpp_best<0x143, 0xC>(k, id);  // row_bcast 31 into rows 2 and 3
+}
+
 template <int WMAX>
 __global__ __launch_bounds__(kSeqThreads) void tree_select_seq(
     const float* __restrict__ part_max, const double* __restrict__ part_sum,
@@ -524,13 +550,9 @@ __global__ __launch_bounds__(kSeqThreads) void tree_select_seq(
 #pragma unroll
     for (int s = 0; s < kSeqSlots; ++s)
       if (seq_better(qk[s], qi[s], bk, bi)) { bk = qk[s]; bi = qi[s]; }
-    for (int o = 32; o > 0; o >>= 1) {
-      const double ok = __shfl_xor(bk, o, kWave);
-      const int oi = __shfl_xor(bi, o, kWave);
-      if (seq_better(ok, oi, bk, bi)) { bk = ok; bi = oi; }
-    }
+    wave_best_to_lane63(bk, bi);
     const int par = pop & 1;
-    if (lane == 0) { red_k[par][wv] = bk; red_i[par][wv] = bi; }
+    if (lane == kWave - 1) { red_k[par][wv] = bk; red_i[par][wv] = bi; }
     __syncthreads();
     bk = red_k[par][0];
     bi = red_i[par][0];
