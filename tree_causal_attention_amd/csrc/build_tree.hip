@@ -125,6 +125,30 @@ __device__ __forceinline__ int co_rank(int o, int la, int lb, Prec prec_ab) {
   return lo;
 }
 
+// Wave argmax of (value, id) under `better`, through DPP lane moves into lane
+// 63, then broadcast: quad swaps, rotations by 4 and 8 inside each row of 16
+// lanes, row broadcasts 15 and 31 (the order is total, so any combination
+// order gives the same winner).  Lanes a move does not reach keep their pair.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ void dpp_better(float& v, int& id) {
+  const float ov = __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, v), __builtin_bit_cast(int, v),
+                                         CTRL, ROW_MASK, 0xF, false));
+  const int oi = __builtin_amdgcn_update_dpp(id, id, CTRL, ROW_MASK, 0xF, false);
+  if (better(ov, oi, v, id)) { v = ov; id = oi; }
+}
+
+__device__ __forceinline__ void wave_best_all(float& v, int& id) {
+  dpp_better<0xB1, 0xF>(v, id);   // quad_perm [1, 0, 3, 2]
+  dpp_better<0x4E, 0xF>(v, id);   // quad_perm [2, 3, 0, 1]
+  dpp_better<0x124, 0xF>(v, id);  // row_ror 4
+  dpp_better<0x128, 0xF>(v, id);  // row_ror 8
+  dpp_better<0x142, 0xA>(v, id);  // row_bcast 15 into rows 1 and 3
+  dpp_better<0x143, 0xC>(v, id);  // row_bcast 31 into rows 2 and 3
+  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
+  id = __builtin_amdgcn_readlane(id, kWave - 1);
+}
+
 // Merge the chunk partials of every depth of sequence seq (one wave a depth;
 // each lane holds one chunk's sorted candidates in registers): lse[d], the
 // top-W (cval, ctok [d * WMAX + r]) and, when part_ent is given, the entropy
@@ -179,11 +203,7 @@ __device__ void merge_depth_partials(const float* __restrict__ part_max,
     for (int r = 0; r < width; ++r) {
       float bv = hv[0];
       int bi = hid[0];
-      for (int o = 32; o > 0; o >>= 1) {
-        const float ov = shfl_xor(bv, o);
-        const int oi = shfl_xor(bi, o);
-        if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
-      }
+      wave_best_all(bv, bi);
       if (hid[0] == bi && bi != INT32_MAX) {  // this lane's head won: pop it
 #pragma unroll
         for (int k = 0; k + 1 < WMAX; ++k) { hv[k] = hv[k + 1]; hid[k] = hid[k + 1]; }
