@@ -353,12 +353,16 @@ def _correlated_case(rng, b, T, V, N, noise):
     return X, Dl, pars, deps, toks, ns
 
 
-@pytest.mark.parametrize("seed,dtype,temp", [(0, "f32", 1.0), (1, "bf16", 1.0), (2, "f32", 0.5),
-                                             (3, "bf16", 1.75), (4, "f32", 0.25),
-                                             (5, "bf16", 0.5)])
-def test_stochastic_small_random_trees(seed, dtype, temp):
+# V = 40: 4-entry row loads and paired cached-row reads; V = 42: paired reads
+# only; V = 37: the one-entry paths throughout
+@pytest.mark.parametrize("seed,dtype,temp,V", [(0, "f32", 1.0, 40), (1, "bf16", 1.0, 40),
+                                               (2, "f32", 0.5, 40), (3, "bf16", 1.75, 40),
+                                               (4, "f32", 0.25, 40), (5, "bf16", 0.5, 40),
+                                               (6, "f32", 1.0, 37), (7, "bf16", 0.7, 37),
+                                               (8, "f32", 1.0, 42), (9, "bf16", 1.3, 42)])
+def test_stochastic_small_random_trees(seed, dtype, temp, V):
     rng = np.random.default_rng(700 + seed)
-    b, T, V, N = 16, 60, 40, 12
+    b, T, N = 16, 60, 12
     X, Dl, pars, deps, toks, ns = _correlated_case(rng, b, T, V, N, noise=0.6)
     ua = rng.random((b, T)).astype(np.float32)
     us = rng.random(b).astype(np.float32)

@@ -150,7 +150,25 @@ template <typename T>
 struct RowView {
   const T* row;
   __device__ __forceinline__ float at(int i) const { return load_as_f32(row, i); }
+  // entries 4j .. 4j + 3 in one load (the row must be 4-entry aligned)
+  __device__ __forceinline__ void at4(int j, float* x) const;
 };
+template <>
+__device__ __forceinline__ void RowView<float>::at4(int j, float* x) const {
+  const float4 v = reinterpret_cast<const float4*>(row)[j];
+  x[0] = v.x;
+  x[1] = v.y;
+  x[2] = v.z;
+  x[3] = v.w;
+}
+template <>
+__device__ __forceinline__ void RowView<uint16_t>::at4(int j, float* x) const {
+  const uint2 v = reinterpret_cast<const uint2*>(row)[j];
+  x[0] = bf16_bits_to_f32(static_cast<uint16_t>(v.x & 0xFFFFu));
+  x[1] = bf16_bits_to_f32(static_cast<uint16_t>(v.x >> 16));
+  x[2] = bf16_bits_to_f32(static_cast<uint16_t>(v.y & 0xFFFFu));
+  x[3] = bf16_bits_to_f32(static_cast<uint16_t>(v.y >> 16));
+}
 
 // fp64 block sum (every thread gets the result); red: kStWaves doubles
 __device__ __forceinline__ double block_sum(double v, double* red) {
@@ -195,23 +213,73 @@ __device__ void row_stats(RowView<T> r, int vocab, double tinv, float* m_out, do
                           int* redi) {
   float m = -INFINITY;
   int b = 0;
-  for (int i0 = threadIdx.x; i0 < vocab; i0 += kStThreads * kStUnroll) {
-    float x[kStUnroll];
+  // 4-entry loads when the row allows them (one load request per 4 entries:
+  // a single workgroup streams the row, so its request rate sets the pace)
+  const bool vec = (vocab & 3) == 0 && (reinterpret_cast<uintptr_t>(r.row) & 15) == 0 &&
+                   (reinterpret_cast<uintptr_t>(e_out) & 15) == 0;
+  if (vec) {
+    const int v4 = vocab / 4;
+    for (int j0 = threadIdx.x; j0 < v4; j0 += kStThreads * 2) {
+      float x[2][4];
 #pragma unroll
-    for (int k = 0; k < kStUnroll; ++k) {
-      const int i = i0 + k * kStThreads;
-      x[k] = i < vocab ? r.at(i) : -INFINITY;
+      for (int k = 0; k < 2; ++k) {
+        const int j = j0 + k * kStThreads;
+        if (j < v4) r.at4(j, x[k]);
+        else x[k][0] = x[k][1] = x[k][2] = x[k][3] = -INFINITY;
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (x[k][e] != x[k][e] || x[k][e] == INFINITY) b = 1;
+          m = fmaxf(m, x[k][e]);
+        }
     }
+  } else {
+    for (int i0 = threadIdx.x; i0 < vocab; i0 += kStThreads * kStUnroll) {
+      float x[kStUnroll];
 #pragma unroll
-    for (int k = 0; k < kStUnroll; ++k) {
-      if (x[k] != x[k] || x[k] == INFINITY) b = 1;
-      m = fmaxf(m, x[k]);
+      for (int k = 0; k < kStUnroll; ++k) {
+        const int i = i0 + k * kStThreads;
+        x[k] = i < vocab ? r.at(i) : -INFINITY;
+      }
+#pragma unroll
+      for (int k = 0; k < kStUnroll; ++k) {
+        if (x[k] != x[k] || x[k] == INFINITY) b = 1;
+        m = fmaxf(m, x[k]);
+      }
     }
   }
   m = block_max(m, redf);
   b = block_or(b, redi);
   double z = 0.0;
-  if (!b && m != -INFINITY)
+  if (!b && m != -INFINITY && vec) {
+    const int v4 = vocab / 4;
+    double2* e2 = reinterpret_cast<double2*>(e_out);
+    for (int j0 = threadIdx.x; j0 < v4; j0 += kStThreads * 2) {
+      float x[2][4];
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int j = j0 + k * kStThreads;
+        if (j < v4) r.at4(j, x[k]);
+        else x[k][0] = x[k][1] = x[k][2] = x[k][3] = m;
+      }
+#pragma unroll
+      for (int k = 0; k < 2; ++k) {
+        const int j = j0 + k * kStThreads;
+        if (j < v4) {
+          double e[4];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            e[q] = exp((static_cast<double>(x[k][q]) - static_cast<double>(m)) * tinv);
+            z += e[q];
+          }
+          e2[2 * j] = make_double2(e[0], e[1]);
+          e2[2 * j + 1] = make_double2(e[2], e[3]);
+        }
+      }
+    }
+  } else if (!b && m != -INFINITY)
     for (int i0 = threadIdx.x; i0 < vocab; i0 += kStThreads * kStUnroll) {
       float x[kStUnroll];
 #pragma unroll
@@ -260,6 +328,8 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
   // exp((x - max) / T) of the current target row and of the children's draft row
   double* et = ecache + static_cast<size_t>(seq) * 2 * vocab;
   double* ed = et + vocab;
+  // the cached rows can be read as 16-byte entry pairs
+  const bool pairs = (vocab & 1) == 0 && (reinterpret_cast<uintptr_t>(et) & 15) == 0;
   auto fail = [&](int bits) {
     if (tid == 0) {
       report(err, bits);
@@ -351,16 +421,37 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
       // rejection: c' = c + U / zd, U' = sum_y max(0, et - c' ed)
       const double c_new = c + U / zd;
       double part = 0.0;
-      for (int i0 = tid; i0 < vocab; i0 += kStThreads * kStUnroll) {
-        double a[kStUnroll], q[kStUnroll];
+      if (pairs) {
+        // 16-byte loads of entry pairs, 4 pairs per thread in flight
+        const double2* et2 = reinterpret_cast<const double2*>(et);
+        const double2* ed2 = reinterpret_cast<const double2*>(ed);
+        const int v2 = vocab / 2;
+        for (int i0 = tid; i0 < v2; i0 += kStThreads * (kStUnroll / 2)) {
+          double2 a[kStUnroll / 2], q[kStUnroll / 2];
 #pragma unroll
-        for (int k = 0; k < kStUnroll; ++k) {
-          const int i = i0 + k * kStThreads;
-          a[k] = i < vocab ? et[i] : 0.0;
-          q[k] = i < vocab ? ed[i] : 0.0;
+          for (int k = 0; k < kStUnroll / 2; ++k) {
+            const int i = i0 + k * kStThreads;
+            a[k] = i < v2 ? et2[i] : make_double2(0.0, 0.0);
+            q[k] = i < v2 ? ed2[i] : make_double2(0.0, 0.0);
+          }
+#pragma unroll
+          for (int k = 0; k < kStUnroll / 2; ++k) {
+            part += fmax(0.0, a[k].x - c_new * q[k].x);
+            part += fmax(0.0, a[k].y - c_new * q[k].y);
+          }
         }
+      } else {
+        for (int i0 = tid; i0 < vocab; i0 += kStThreads * kStUnroll) {
+          double a[kStUnroll], q[kStUnroll];
 #pragma unroll
-        for (int k = 0; k < kStUnroll; ++k) part += fmax(0.0, a[k] - c_new * q[k]);
+          for (int k = 0; k < kStUnroll; ++k) {
+            const int i = i0 + k * kStThreads;
+            a[k] = i < vocab ? et[i] : 0.0;
+            q[k] = i < vocab ? ed[i] : 0.0;
+          }
+#pragma unroll
+          for (int k = 0; k < kStUnroll; ++k) part += fmax(0.0, a[k] - c_new * q[k]);
+        }
       }
       const double un = block_sum(part, redd);
       if (un == 0.0) break;  // no mass left: keep the previous distribution
@@ -381,15 +472,36 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
   const int seg = (vocab + kStWaves * kWave - 1) / (kStWaves * kWave) * kWave;
   const int s0 = min(vocab, wv * seg), s1 = min(vocab, s0 + seg);
   double own = 0.0;
-  for (int i0 = s0 + lane; i0 < s1; i0 += kWave * kStUnroll) {
-    double w[kStUnroll];
+  if (pairs) {
+    // 16-byte loads of entry pairs (segments start at even entries; an even
+    // vocabulary ends them at even entries too)
+    const double2* et2 = reinterpret_cast<const double2*>(et);
+    const double2* ed2 = reinterpret_cast<const double2*>(ed);
+    for (int i0 = s0 / 2 + lane; i0 < s1 / 2; i0 += kWave * (kStUnroll / 2)) {
+      double2 a[kStUnroll / 2], q[kStUnroll / 2];
 #pragma unroll
-    for (int k = 0; k < kStUnroll; ++k) {
-      const int i = i0 + k * kWave;
-      w[k] = i < s1 ? weight(i) : 0.0;
+      for (int k = 0; k < kStUnroll / 2; ++k) {
+        const int i = i0 + k * kWave;
+        a[k] = i < s1 / 2 ? et2[i] : make_double2(0.0, 0.0);
+        q[k] = i < s1 / 2 ? ed2[i] : make_double2(0.0, 0.0);
+      }
+#pragma unroll
+      for (int k = 0; k < kStUnroll / 2; ++k) {
+        own += c == 0.0 ? a[k].x : fmax(0.0, a[k].x - c * q[k].x);
+        own += c == 0.0 ? a[k].y : fmax(0.0, a[k].y - c * q[k].y);
+      }
     }
+  } else {
+    for (int i0 = s0 + lane; i0 < s1; i0 += kWave * kStUnroll) {
+      double w[kStUnroll];
 #pragma unroll
-    for (int k = 0; k < kStUnroll; ++k) own += w[k];
+      for (int k = 0; k < kStUnroll; ++k) {
+        const int i = i0 + k * kWave;
+        w[k] = i < s1 ? weight(i) : 0.0;
+      }
+#pragma unroll
+      for (int k = 0; k < kStUnroll; ++k) own += w[k];
+    }
   }
   for (int o = 32; o > 0; o >>= 1) own += __shfl_xor(own, o, kWave);
   if (lane == 0) wsum[wv] = own;
