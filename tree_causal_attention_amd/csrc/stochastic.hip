@@ -36,6 +36,7 @@ constexpr int kStWaves = kStThreads / kWave;
 // Passes over the vocabulary load kStUnroll entries per thread before using
 // them: one workgroup streams a whole row, so its loads in flight set the pace.
 constexpr int kStUnroll = 8;
+constexpr int kBonusBlocks = 4;  // blocks per wave segment of the bonus draw
 constexpr int kPreThreads = 256;
 constexpr int kPreChunk = kPreThreads * 16;  // entries of one pre-pass workgroup
 
@@ -317,7 +318,8 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
   __shared__ float redf[kStWaves];
   __shared__ double redd[kStWaves];
   __shared__ int redi[kStWaves];
-  __shared__ double wsum[kStWaves], wpre[kStWaves];
+  __shared__ double bsum[kStWaves * kBonusBlocks], bpre[kStWaves * kBonusBlocks];
+  __shared__ int owner_s;
   __shared__ int path[64];
   __shared__ int pick;
   __shared__ double thr_s;
@@ -465,75 +467,94 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
     __syncthreads();  // every thread is done with et before the next row overwrites it
   }
   // ---- bonus: inverse-CDF draw over the residual weights of the current node.
-  // Wave w owns a contiguous segment of the vocabulary (lanes read it
-  // coalesced); segment sums give an exclusive prefix, and the wave whose
-  // interval holds u * total scans its segment 64 entries at a time.
+  // Wave w owns a contiguous segment of the vocabulary, cut into kBonusBlocks
+  // blocks (lanes read them coalesced).  One exclusive prefix over the block
+  // sums in (wave, block) order finds the block whose interval holds
+  // u * total (the intervals tile [0, total) exactly: they come from the same
+  // fp64 additions), and that block's wave scans it 64 entries at a time.
   auto weight = [&](int i) -> double { return c == 0.0 ? et[i] : fmax(0.0, et[i] - c * ed[i]); };
   const int seg = (vocab + kStWaves * kWave - 1) / (kStWaves * kWave) * kWave;
   const int s0 = min(vocab, wv * seg), s1 = min(vocab, s0 + seg);
-  double own = 0.0;
-  if (pairs) {
-    // 16-byte loads of entry pairs (segments start at even entries; an even
-    // vocabulary ends them at even entries too)
-    const double2* et2 = reinterpret_cast<const double2*>(et);
-    const double2* ed2 = reinterpret_cast<const double2*>(ed);
-    for (int i0 = s0 / 2 + lane; i0 < s1 / 2; i0 += kWave * (kStUnroll / 2)) {
-      double2 a[kStUnroll / 2], q[kStUnroll / 2];
+  const int blen = ((seg + kBonusBlocks - 1) / kBonusBlocks + kWave - 1) / kWave * kWave;
+  double own[kBonusBlocks];
 #pragma unroll
-      for (int k = 0; k < kStUnroll / 2; ++k) {
-        const int i = i0 + k * kWave;
-        a[k] = i < s1 / 2 ? et2[i] : make_double2(0.0, 0.0);
-        q[k] = i < s1 / 2 ? ed2[i] : make_double2(0.0, 0.0);
+  for (int bb = 0; bb < kBonusBlocks; ++bb) {
+    const int b0 = min(s1, s0 + bb * blen), b1 = min(s1, b0 + blen);
+    double acc = 0.0;
+    if (pairs) {
+      // 16-byte loads of entry pairs (blocks start and, with an even
+      // vocabulary, end at even entries)
+      const double2* et2 = reinterpret_cast<const double2*>(et);
+      const double2* ed2 = reinterpret_cast<const double2*>(ed);
+      for (int i0 = b0 / 2 + lane; i0 < b1 / 2; i0 += kWave * (kStUnroll / 2)) {
+        double2 a[kStUnroll / 2], q[kStUnroll / 2];
+#pragma unroll
+        for (int k = 0; k < kStUnroll / 2; ++k) {
+          const int i = i0 + k * kWave;
+          a[k] = i < b1 / 2 ? et2[i] : make_double2(0.0, 0.0);
+          q[k] = i < b1 / 2 ? ed2[i] : make_double2(0.0, 0.0);
+        }
+#pragma unroll
+        for (int k = 0; k < kStUnroll / 2; ++k) {
+          acc += c == 0.0 ? a[k].x : fmax(0.0, a[k].x - c * q[k].x);
+          acc += c == 0.0 ? a[k].y : fmax(0.0, a[k].y - c * q[k].y);
+        }
       }
+    } else {
+      for (int i0 = b0 + lane; i0 < b1; i0 += kWave * kStUnroll) {
+        double w[kStUnroll];
 #pragma unroll
-      for (int k = 0; k < kStUnroll / 2; ++k) {
-        own += c == 0.0 ? a[k].x : fmax(0.0, a[k].x - c * q[k].x);
-        own += c == 0.0 ? a[k].y : fmax(0.0, a[k].y - c * q[k].y);
+        for (int k = 0; k < kStUnroll; ++k) {
+          const int i = i0 + k * kWave;
+          w[k] = i < b1 ? weight(i) : 0.0;
+        }
+#pragma unroll
+        for (int k = 0; k < kStUnroll; ++k) acc += w[k];
       }
     }
-  } else {
-    for (int i0 = s0 + lane; i0 < s1; i0 += kWave * kStUnroll) {
-      double w[kStUnroll];
-#pragma unroll
-      for (int k = 0; k < kStUnroll; ++k) {
-        const int i = i0 + k * kWave;
-        w[k] = i < s1 ? weight(i) : 0.0;
-      }
-#pragma unroll
-      for (int k = 0; k < kStUnroll; ++k) own += w[k];
-    }
+    own[bb] = acc;
   }
-  for (int o = 32; o > 0; o >>= 1) own += __shfl_xor(own, o, kWave);
-  if (lane == 0) wsum[wv] = own;
+#pragma unroll
+  for (int bb = 0; bb < kBonusBlocks; ++bb) {
+    double v = own[bb];
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+    if (lane == 0) bsum[wv * kBonusBlocks + bb] = v;
+  }
   __syncthreads();
   if (tid == 0) {
     double tot = 0.0;
-    for (int k = 0; k < kStWaves; ++k) {
-      wpre[k] = tot;  // exclusive prefix
-      tot += wsum[k];
+    for (int k = 0; k < kStWaves * kBonusBlocks; ++k) {
+      bpre[k] = tot;  // exclusive prefix
+      tot += bsum[k];
     }
-    thr_s = static_cast<double>(u_sample[seq]) * tot;
+    const double thr = static_cast<double>(u_sample[seq]) * tot;
+    int o = -1;
+    for (int k = 0; k < kStWaves * kBonusBlocks && o < 0; ++k)
+      if (bpre[k] <= thr && bpre[k] + bsum[k] > thr) o = k;
+    thr_s = thr;
+    owner_s = o;
     pick = -1;
   }
   __syncthreads();
   const double thr = thr_s;
-  // The intervals [wpre_k, wpre_k + wsum_k) tile [0, tot) exactly (the same
-  // fp64 additions as the prefix), so exactly one wave owns thr.
-  if (s0 < s1 && wpre[wv] <= thr && wpre[wv] + wsum[wv] > thr) {
-    double carry = wpre[wv];
+  const int owner = owner_s;
+  if (owner >= 0 && wv == owner / kBonusBlocks) {
+    const int bb = owner % kBonusBlocks;
+    const int b0 = min(s1, s0 + bb * blen), b1 = min(s1, b0 + blen);
+    double carry = bpre[owner];
     int y = -1, last_pos = -1;
     // 64-entry chunks in order, kStUnroll chunks loaded at a time
-    for (int b0 = s0; b0 < s1 && y < 0; b0 += kWave * kStUnroll) {
+    for (int c0 = b0; c0 < b1 && y < 0; c0 += kWave * kStUnroll) {
       double wk[kStUnroll];
 #pragma unroll
       for (int k = 0; k < kStUnroll; ++k) {
-        const int i = b0 + k * kWave + lane;
-        wk[k] = i < s1 ? weight(i) : 0.0;
+        const int i = c0 + k * kWave + lane;
+        wk[k] = i < b1 ? weight(i) : 0.0;
       }
 #pragma unroll
       for (int k = 0; k < kStUnroll; ++k) {
-        const int r0 = b0 + k * kWave;
-        if (y >= 0 || r0 >= s1) break;  // wave-uniform
+        const int r0 = c0 + k * kWave;
+        if (y >= 0 || r0 >= b1) break;  // wave-uniform
         const double w = wk[k];
         double incl = w;  // inclusive prefix over the 64 lanes
         for (int o = 1; o < kWave; o <<= 1) {
