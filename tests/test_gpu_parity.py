@@ -447,3 +447,28 @@ def test_build_tree_ties_at_the_cut(seed):
         for s in range(b):
             ref = O.build_tree(L[s], W, Bb, int(roots[s]), check_exact=False)
             _assert_tree_equal(g, ref, s, f"ties seed {seed} B={Bb}")
+
+
+@pytest.mark.parametrize("case", [
+    (2, [100, 20], [257, 256], 257, 8, 1, 128, "bf16"),   # nothing split: direct writes
+    (1, [3000], [300], 300, 8, 2, 128, "bf16"),          # split tiles, merged
+    (2, [31, 150], [20, 9], 20, 6, 3, 64, "f32"),        # fp32 path
+], ids=["direct", "merged", "f32"])
+def test_attention_without_lse_is_identical(case):
+    """lse is optional: leaving it out changes no output bit."""
+    b, prefixes, ns, T, hq, hkv, D, dtype = case
+    rng = np.random.default_rng(4242 + T)
+    q, k, v, table, num_pages, parents = _attn_case(rng, b, prefixes, ns, T, hq, hkv, D, dtype)
+    d = dev()
+    par = torch.tensor(parents, dtype=torch.int32, device=d)
+    nn = torch.tensor(ns, dtype=torch.int32, device=d)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    anc = B.jt_tree_meta(par, nn, err=err)
+    args = (q.to(d), k.to(d), v.to(d), nn, torch.tensor(prefixes, dtype=torch.int32, device=d),
+            torch.from_numpy(table).to(d), num_pages, anc, 0.125)
+    o1, l1 = B.jt_tree_attention(*args, err=err, with_lse=True)
+    o2, l2 = B.jt_tree_attention(*args, err=err, with_lse=False)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0 and l1 is not None and l2 is None
+    for s in range(b):
+        assert torch.equal(o1[s, :ns[s]], o2[s, :ns[s]])
