@@ -472,3 +472,37 @@ def test_attention_without_lse_is_identical(case):
     assert int(err.item()) == 0 and l1 is not None and l2 is None
     for s in range(b):
         assert torch.equal(o1[s, :ns[s]], o2[s, :ns[s]])
+
+
+def test_step_with_optional_pointers_left_out():
+    """The whole step with no error word, no score output and no lse gives
+    the same results as with them (the optional pointers only add outputs)."""
+    w = WL.WORKLOADS["qwen3_8b_b16"]
+    x = WL.make_inputs(w)
+    d = dev()
+    draft, target, root = x.draft.to(d), x.target.to(d), x.root_token.to(d)
+    args_attn = (x.q.to(d), x.k_pool.to(d), x.v_pool.to(d))
+    pre, tab = x.prefix_len.to(d), x.page_table.to(d)
+
+    def step(err, opt):
+        t = B.jt_build_tree(draft, w.width_w, w.budget_b, root, err=err, with_score=opt)
+        anc = B.jt_tree_meta(t["parent"], t["n_nodes"], err=err)
+        o, lse = B.jt_tree_attention(*args_attn, t["n_nodes"], pre, tab, x.num_pages, anc,
+                                     w.scale, err=err, with_lse=opt)
+        acc = B.jt_accept(target, w.depth_n, t["parent"], t["token"], t["depth"], t["n_nodes"],
+                          err=err)
+        torch.cuda.synchronize()
+        return t, anc, o, acc
+
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    t1, a1, o1, acc1 = step(err, True)
+    assert int(err.item()) == 0
+    t2, a2, o2, acc2 = step(None, False)
+    assert t2["score"] is None
+    for k in ("parent", "token", "depth", "n_nodes"):
+        assert torch.equal(t1[k], t2[k]), k
+    assert torch.equal(a1, a2)
+    n = int(t1["n_nodes"][0])
+    assert torch.equal(o1[:, :n], o2[:, :n])
+    for r1, r2 in zip(acc1, acc2):
+        assert torch.equal(r1, r2)
