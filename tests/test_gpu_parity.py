@@ -506,3 +506,38 @@ def test_step_with_optional_pointers_left_out():
     assert torch.equal(o1[:, :n], o2[:, :n])
     for r1, r2 in zip(acc1, acc2):
         assert torch.equal(r1, r2)
+
+
+def test_step_on_a_side_stream():
+    """Every call enqueues on the caller's stream: the step run on a second
+    (default-priority) stream gives the default stream's results."""
+    w = WL.WORKLOADS["qwen3_8b_b16"]
+    x = WL.make_inputs(w, instance=1)
+    d = dev()
+    draft, target, root = x.draft.to(d), x.target.to(d), x.root_token.to(d)
+    q, k, v = x.q.to(d), x.k_pool.to(d), x.v_pool.to(d)
+    pre, tab = x.prefix_len.to(d), x.page_table.to(d)
+
+    def step():
+        err = torch.zeros(1, dtype=torch.int32, device=d)
+        t = B.jt_build_tree(draft, w.width_w, w.budget_b, root, err=err)
+        anc = B.jt_tree_meta(t["parent"], t["n_nodes"], err=err)
+        o, lse = B.jt_tree_attention(q, k, v, t["n_nodes"], pre, tab, x.num_pages, anc, w.scale,
+                                     err=err)
+        acc = B.jt_accept(target, w.depth_n, t["parent"], t["token"], t["depth"], t["n_nodes"],
+                          err=err)
+        return [t["parent"], t["token"], t["n_nodes"], anc, o, lse, *acc, err]
+
+    ref = step()
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        got = step()
+    torch.cuda.synchronize()
+    assert int(ref[-1].item()) == 0 and int(got[-1].item()) == 0
+    n = int(ref[2][0])
+    for i, (a, b_) in enumerate(zip(ref, got)):
+        if i in (4, 5):  # attention outputs: rows past n_nodes are not written
+            a, b_ = a[:, :n], b_[:, :n]
+        assert torch.equal(a, b_), i
