@@ -541,3 +541,50 @@ def test_step_on_a_side_stream():
         if i in (4, 5):  # attention outputs: rows past n_nodes are not written
             a, b_ = a[:, :n], b_[:, :n]
         assert torch.equal(a, b_), i
+
+
+def test_step_captured_in_a_graph():
+    """The step captures into a HIP graph: the library calls enqueue kernels
+    only (no allocation, memset or host synchronisation; the binding's output
+    tensors come from the graph's memory pool).  Three replays, with eager
+    work and synchronisations between them, each reproduce the eager results."""
+    w = WL.WORKLOADS["qwen3_8b_b16"]
+    x = WL.make_inputs(w, instance=2)
+    d = dev()
+    draft, target, root = x.draft.to(d), x.target.to(d), x.root_token.to(d)
+    q, k, v = x.q.to(d), x.k_pool.to(d), x.v_pool.to(d)
+    pre, tab = x.prefix_len.to(d), x.page_table.to(d)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+
+    def step():
+        t = B.jt_build_tree(draft, w.width_w, w.budget_b, root, err=err)
+        anc = B.jt_tree_meta(t["parent"], t["n_nodes"], err=err)
+        o, lse = B.jt_tree_attention(q, k, v, t["n_nodes"], pre, tab, x.num_pages, anc, w.scale,
+                                     err=err)
+        acc = B.jt_accept(target, w.depth_n, t["parent"], t["token"], t["depth"], t["n_nodes"],
+                          err=err)
+        return [t["parent"], t["token"], t["n_nodes"], anc, o, lse, *acc]
+
+    ref = [r.clone() for r in step()]
+    torch.cuda.synchronize()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # warm-up on the capture stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = step()
+    n = int(ref[2][0])
+    for _ in range(3):
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert int(err.item()) == 0
+        for i, (a, b_) in enumerate(zip(ref, outs)):
+            if i in (4, 5):
+                a, b_ = a[:, :n], b_[:, :n]
+            assert torch.equal(a, b_), i
