@@ -588,3 +588,42 @@ def test_step_captured_in_a_graph():
             if i in (4, 5):
                 a, b_ = a[:, :n], b_[:, :n]
             assert torch.equal(a, b_), i
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_attention_bad_page_and_bad_prefix(dtype):
+    """A page id outside the pool is reported and its keys and values read as
+    zero (the oracle sees an all-zero page there); a sequence whose prefix
+    and tree overflow its page table is reported and skipped (rows untouched);
+    the other sequences are unaffected."""
+    rng = np.random.default_rng(99 if dtype == "bf16" else 98)
+    b, prefixes, ns, T, hq, hkv, D = 3, [200, 150, 100], [30, 30, 30], 30, 8, 2, 64
+    q, k, v, table, num_pages, parents = _attn_case(rng, b, prefixes, ns, T, hq, hkv, D, dtype)
+    bad_table = table.copy()
+    bad_table[1, 3] = num_pages + 5          # positions 48..63 of sequence 1 (prefix)
+    gpu_prefixes = [200, 150, table.shape[1] * 16]  # sequence 2 overflows its table
+    d = dev()
+    par = torch.tensor(parents, dtype=torch.int32, device=d)
+    nn = torch.tensor(ns, dtype=torch.int32, device=d)
+    err = torch.zeros(1, dtype=torch.int32, device=d)
+    anc = B.jt_tree_meta(par, nn, err=err)
+    out = torch.full(q.shape, 7.0, dtype=q.dtype, device=d)
+    o, lse = B.jt_tree_attention(q.to(d), k.to(d), v.to(d), nn,
+                                 torch.tensor(gpu_prefixes, dtype=torch.int32, device=d),
+                                 torch.from_numpy(bad_table).to(d), num_pages, anc, 1 / np.sqrt(D),
+                                 err=err, out=out)
+    torch.cuda.synchronize()
+    assert int(err.item()) == (B.DERR_BAD_PAGE | B.DERR_BAD_PREFIX)
+    og, lg = as_f64(o), to_np(lse).astype(np.float64)
+    kf, vf, qf = k.float().numpy(), v.float().numpy(), q.float().numpy()
+    # the oracle reads an appended all-zero page where the bad id points
+    kz = np.concatenate([kf, np.zeros_like(kf[:1])])
+    vz = np.concatenate([vf, np.zeros_like(vf[:1])])
+    zero_table = table.copy()
+    zero_table[1, 3] = num_pages
+    for s in (0, 1):
+        ro, rl = O.tree_attention_seq_fast(qf[s], kz, vz, zero_table[s], prefixes[s], parents[s],
+                                           ns[s], 1 / np.sqrt(D))
+        check_attention(og[s, :ns[s]], ro, dtype, f"seq {s}")
+        check_lse(lg[s, :ns[s]], rl, dtype, f"seq {s}")
+    assert (og[2] == 7.0).all(), "the skipped sequence must not be written"

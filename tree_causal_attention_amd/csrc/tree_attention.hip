@@ -677,17 +677,19 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32(
   const int key_end = P + node + 1;
   for (int t0 = 0; t0 < key_end; t0 += kWave) {
     const int t = t0 + lane;
-    bool vis = t < key_end && (t < P || ((arow[(t - P) >> 5] >> ((t - P) & 31)) & 1u));
+    const bool vis = t < key_end && (t < P || ((arow[(t - P) >> 5] >> ((t - P) & 31)) & 1u));
+    // a bad page id is reported and its keys and values read as zero
     const float* krow = nullptr;
     if (vis) {
       const int page = ptab[t / kPage];
-      if (page < 0 || page >= num_pages) { report(err, JT_DERR_BAD_PAGE); vis = false; }
+      if (page < 0 || page >= num_pages) report(err, JT_DERR_BAD_PAGE);
       else krow = k_pool + page * ps + g * hs + (t % kPage) * D;
     }
     float sc = -INFINITY;
     if (vis) {
       float dot = 0.0f;
-      for (int d = 0; d < D; ++d) dot = fmaf(qs[d], krow[d], dot);
+      if (krow)
+        for (int d = 0; d < D; ++d) dot = fmaf(qs[d], krow[d], dot);
       sc = dot * scale;
     }
     float mx = sc;
@@ -707,6 +709,7 @@ __global__ __launch_bounds__(kWave) void tree_attn_f32(
       if (pj == 0.0f) continue;  // uniform across the wave
       const int tj = t0 + j;
       const int page = ptab[tj / kPage];
+      if (page < 0 || page >= num_pages) continue;  // a zero value row adds nothing
       const float* vrow = v_pool + page * ps + g * hs + (tj % kPage) * D;
 #pragma unroll
       for (int k = 0; k < PER; ++k) o[k] = fmaf(pj, vrow[lane + k * kWave], o[k]);
