@@ -627,3 +627,29 @@ def test_attention_bad_page_and_bad_prefix(dtype):
         check_attention(og[s, :ns[s]], ro, dtype, f"seq {s}")
         check_lse(lg[s, :ns[s]], rl, dtype, f"seq {s}")
     assert (og[2] == 7.0).all(), "the skipped sequence must not be written"
+
+
+def test_accept_bad_depth_reported():
+    """depth[v] != depth[parent] + 1, or a node deeper than depth_n: reported,
+    that sequence's outputs are zero / -1, the others are unaffected."""
+    rng = np.random.default_rng(515)
+    T, V, N = 12, 5, 4
+    p = [-1, 0, 1, 2, 3, 0, 5, -1, -1, -1, -1, -1]   # a chain of depth 4, then node 6 at depth 2
+    dd = [0, 1, 2, 3, 4, 1, 2, -1, -1, -1, -1, -1]
+    parents = [p, p, p]
+    bad_rel = list(dd)
+    bad_rel[6] = 3                                   # its parent 5 has depth 1
+    depths = [dd, bad_rel, dd]
+    ns = [7, 7, 7]
+    tokens = [[int(x) for x in rng.integers(0, V, T)] for _ in range(3)]
+    X = torch.from_numpy(rng.standard_normal((3, T, V)).astype(np.float32))
+    alen, anodes, bonus, err = _gpu_accept(X, N, parents, tokens, depths, ns)
+    assert err == B.DERR_BAD_DEPTH
+    assert (alen[1], bonus[1]) == (0, -1) and (anodes[1] == -1).all()
+    for s in (0, 2):
+        L, nodes, bb = O.accept(X[s].numpy(), parents[s], tokens[s], depths[s], ns[s], N)
+        assert (alen[s], bonus[s]) == (L, bb) and np.array_equal(anodes[s], nodes)
+    # with depth_n = 3 the depth-4 node of every sequence is too deep
+    alen3, anodes3, bonus3, err3 = _gpu_accept(X, 3, parents, tokens, depths, ns)
+    assert err3 == B.DERR_BAD_DEPTH
+    assert (alen3 == 0).all() and (bonus3 == -1).all() and (anodes3 == -1).all()
