@@ -421,9 +421,11 @@ def test_accept_bf16_logits():
     assert alen[0] == 4
 
 
-@pytest.mark.parametrize("N,W,Bb", [(24, 2, 100), (40, 1, 60), (17, 3, 200)])
+@pytest.mark.parametrize("N,W,Bb", [(24, 2, 100), (40, 1, 60), (17, 3, 200), (64, 1, 100),
+                                    (64, 2, 120), (8, 16, 200)])
 def test_build_tree_deep(N, W, Bb):
-    """Depths past 16 take the kernel variant sized for up to 64 levels."""
+    """Depths past 16 take the kernel variant sized for up to 64 levels; the
+    largest depth (64) and width (16) the call takes."""
     rng = np.random.default_rng(N * 100 + W)
     L = (rng.standard_normal((2, N, 500)) * rng.uniform(1, 10)).astype(np.float32)
     roots = np.array([3, 4], dtype=np.int32)
