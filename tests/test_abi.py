@@ -59,6 +59,10 @@ def test_build_tree_validation(lib):
     assert call(w=17, v=1000) == B.JT_ERR_UNSUPPORTED    # W > 16
     assert call(bb=1024) == B.JT_ERR_UNSUPPORTED         # B + 1 > 1024
     assert call(n=65) == B.JT_ERR_UNSUPPORTED
+    # the selection state of 64 levels of up to 300 nodes does not fit one
+    # workgroup's LDS; 64 levels of up to 120 do (checked before any launch)
+    assert call(n=64, v=500, w=2, bb=300) == B.JT_ERR_UNSUPPORTED
+    assert call(n=64, v=500, w=2, bb=120, b=0) == B.JT_OK
     assert call(ptr=0) == B.JT_ERR_INVALID_ARG           # null pointers
     assert call(ws_bytes=0) == B.JT_ERR_WORKSPACE        # workspace too small
     assert call(b=0) == B.JT_OK                          # empty batch: nothing to do
