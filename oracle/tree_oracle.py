@@ -526,8 +526,17 @@ def sample_index(p, u):
     return int(np.searchsorted(c, t, side="right"))
 
 
+def _check_stochastic_rows(rows):
+    for arr in rows:
+        arr = np.asarray(arr, dtype=np.float64)
+        if np.isnan(arr).any() or np.isposinf(arr).any():
+            raise OracleInputError("logits must not be NaN or +inf")
+        if (arr.max(axis=-1) == -np.inf).any():
+            raise OracleInputError("every logit row needs a finite entry")
+
+
 def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes, n_depth,
-                      temperature, u_accept, u_sample, margins=None):
+                      temperature, u_accept, u_sample, margins=None, draft_mode="topw"):
     """Stochastic (temperature T > 0) verification of one sequence's tree.
 
     The SD overview (chooseai.io/news/6515), section on what speculative
@@ -537,17 +546,32 @@ def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes
     min(1, p(x) / q(x)); on rejection draw from norm(max(0, p - q)).  The
     output then has the target's distribution.
 
-    Readings for a tree (the pages state the rule for one token):
-    * p at node u is softmax(target row u / T); q for a child at depth d is
-      softmax(draft row d / T) (candidates are per depth).
-    * At an accepted node, its children are tried in node-index order (= their
-      candidate rank).  Child v (token x) is accepted iff
-      u_accept[v] * q(x) < p(x), with p the current target distribution; on
-      rejection p becomes norm(max(0, p - q)) and the next child is tried.
-    * An accepted child becomes the current node (p = its own target row).
+    What q is depends on how the tree's tokens were proposed, so the rule
+    takes the proposal as a mode:
+
+    * ``draft_mode="topw"`` (the trees the build step makes).  The JetSpec
+      news piece (tree-construction paragraph) and explainer (section 五)
+      build each depth's siblings as the W most likely draft tokens: they are
+      chosen, not sampled, so the proposal behind the k-th sibling, given
+      that the earlier ones were rejected, is the point mass on its token.
+      With q = point mass at x the rule reads: accept x with probability
+      min(1, p(x) / 1) = p(x); on rejection the residual norm(max(0, p - q))
+      is p with x removed, renormalised.  The draft logits are not used.
+    * ``draft_mode="sampled"``.  Every child of a node was drawn
+      independently from q = softmax(draft row of its depth / T); the rule
+      is applied child after child with that same q, each rejection replacing
+      p by norm(max(0, p - q)).  This is lossless only under that sampling
+      assumption (it is not for top-W siblings).
+
+    Common readings (the pages state the rule for one token):
+    * p at node u is softmax(target row u / T).
+    * The children of the current node are tried in node-index order (their
+      candidate rank).  Child v with token x is accepted iff
+      u_accept[v] * q(x) < p(x) (topw: u_accept[v] < p(x)), p being the
+      current distribution.  An accepted child becomes the current node.
     * When no child is accepted (or there is none) the walk stops and the
       bonus token is drawn from the current p with u_sample (sample_index).
-    * If a rejection leaves no mass (max(0, p - q) == 0 everywhere) the
+    * If a rejection leaves no mass (the residual sums to zero) the
       remaining children are not tried and the bonus is drawn from p as it
       was before that rejection.
     Randomness is passed in: u_accept [n_nodes] (one uniform per node, used
@@ -561,13 +585,14 @@ def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes
     in another order may take a different decision only where this is at the
     rounding level.
     """
+    if draft_mode not in ("topw", "sampled"):
+        raise OracleInputError(f"unknown draft mode {draft_mode!r}")
     X = np.asarray(target_logits)
-    Dl = np.asarray(draft_logits)
-    for arr in (np.asarray(X[:n_nodes], dtype=np.float64), np.asarray(Dl, dtype=np.float64)):
-        if np.isnan(arr).any() or np.isposinf(arr).any():
-            raise OracleInputError("logits must not be NaN or +inf")
-        if (arr.max(axis=-1) == -np.inf).any():
-            raise OracleInputError("every logit row needs a finite entry")
+    if draft_mode == "sampled":
+        Dl = np.asarray(draft_logits)
+        _check_stochastic_rows([X[:n_nodes], Dl])
+    else:
+        _check_stochastic_rows([X[:n_nodes]])
     if not (float(temperature) > 0.0 and np.isfinite(temperature)):
         raise OracleInputError("temperature must be positive and finite")
     u = 0
@@ -577,8 +602,12 @@ def accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes
         kids = [v for v in range(1, n_nodes) if int(parent[v]) == u]
         nxt = None
         for v in kids:
-            q = softmax_t(Dl[int(depth[v]) - 1], temperature)
             x = int(token[v])
+            if draft_mode == "sampled":
+                q = softmax_t(Dl[int(depth[v]) - 1], temperature)
+            else:
+                q = np.zeros_like(p)
+                q[x] = 1.0
             lhs = float(u_accept[v]) * q[x]
             if margins is not None:
                 den = max(p[x], lhs)

@@ -1,4 +1,4 @@
-"""Pins for the oracle's margin acceptance and KV commit.
+"""Pins for the oracle's margin acceptance, KV commit and stochastic verification.
 
 Margin acceptance: the page's worked example (tests/golden), reduction to
 greedy acceptance at a zero margin when rows have no ties, path enumeration
@@ -153,13 +153,25 @@ def test_commit_then_decode_equals_tree_attention(seed):
 # ------------------------------------------------------- stochastic verify
 
 def test_stochastic_hand_example():
+    """The i.i.d. proposal mode on one drafted token (q given explicitly)."""
     g = json.load(open(os.path.join(GOLDEN, "stochastic_example.json")))
     X = np.log(np.array(g["target_probs"]))
     Dl = np.log(np.array(g["draft_probs"]))
     for c in g["cases"]:
         ua = np.array([0.0, c["u_accept"]])
         L, nodes, bonus = O.accept_stochastic(X, Dl, g["parent"], g["token"], g["depth"], 2, 1,
-                                              1.0, ua, c["u_sample"])
+                                              1.0, ua, c["u_sample"], draft_mode="sampled")
+        assert (L, nodes.tolist(), bonus) == (c["accept_len"], c["accept_nodes"], c["bonus"]), c
+
+
+def test_stochastic_topw_hand_example():
+    """Top-W siblings (point-mass proposals): the hand-worked four-node tree."""
+    g = json.load(open(os.path.join(GOLDEN, "stochastic_topw_example.json")))
+    X = np.log(np.array(g["target_probs"]))
+    for c in g["cases"]:
+        L, nodes, bonus = O.accept_stochastic(X, None, g["parent"], g["token"], g["depth"], 4,
+                                              g["n_depth"], 1.0, np.array(c["u_accept"]),
+                                              c["u_sample"])
         assert (L, nodes.tolist(), bonus) == (c["accept_len"], c["accept_nodes"], c["bonus"]), c
 
 
@@ -168,11 +180,107 @@ def test_sample_index_is_inverse_cdf():
     assert [O.sample_index(p, u) for u in (0.0, 0.2, 0.26, 0.74, 0.76, 0.999)] == [1, 1, 3, 3, 4, 4]
 
 
+@pytest.mark.parametrize("T", [0.25, 0.7, 1.0, 1.75])
+def test_softmax_t_against_scipy(T):
+    """softmax(x / T) against scipy's own routine, rows with -inf entries too."""
+    from scipy.special import softmax
+    rng = np.random.default_rng(int(T * 100))
+    for _ in range(5):
+        x = rng.standard_normal(37) * 4.0
+        x[rng.integers(0, 37, 3)] = -np.inf
+        got = O.softmax_t(x, T)
+        ref = softmax(x / T)
+        assert np.allclose(got, ref, rtol=1e-12, atol=1e-300)
+        assert abs(got.sum() - 1.0) < 1e-12
+
+
+@pytest.mark.parametrize("theta,T", [(0.8, 0.5), (0.8, 1.0), (0.3, 1.75), (0.95, 0.25)])
+def test_margin_from_ratio_at_temperature(theta, T):
+    """A row whose second logit sits exactly at the margin below the first has
+    probability ratio theta under softmax(x / T) (scipy), whatever T is."""
+    from scipy.special import softmax
+    m = O.margin_from_ratio(theta, T)
+    p = softmax(np.array([0.0, m, -3.0]) / T)
+    assert abs(p[1] / p[0] - theta) < 1e-12
+    if (theta, T) == (0.8, 0.5):
+        assert abs(m - (-0.11157177565710485)) < 1e-15  # 0.5 * ln 0.8 by hand
+
+
+def _first_tokens(tgt, par, toks, dep, n, N, T, rng, trials, mode, dft=None):
+    """Runs the walk `trials` times; returns (first emitted token, second emitted
+    token or -1, node accepted first or 0) per trial."""
+    out = np.empty((trials, 3), dtype=np.int64)
+    for i in range(trials):
+        ua = rng.random(n)
+        us = rng.random()
+        L, nodes, bonus = O.accept_stochastic(tgt, dft, par, toks, dep, n, N, T, ua, us,
+                                              draft_mode=mode)
+        emitted = [toks[v] for v in nodes[:L]] + [bonus]
+        out[i] = (emitted[0], emitted[1] if len(emitted) > 1 else -1, nodes[0] if L else 0)
+    return out
+
+
+def _chi2(counts, p):
+    expected = p * counts.sum()
+    keep = expected > 0
+    assert counts[~keep].sum() == 0, (counts, p)
+    return float(((counts[keep] - expected[keep]) ** 2 / expected[keep]).sum())
+
+
+def test_stochastic_topw_counterexample_is_lossless():
+    """q = [.5, .3, .2], p = [.2, .2, .6], siblings = the top-2 draft tokens
+    [0, 1]: the emitted token must follow p (the i.i.d. rule gives [.4, 0, .6])."""
+    rng = np.random.default_rng(7)
+    tgt = np.log(np.array([[0.2, 0.2, 0.6]] * 3))
+    dft = np.log(np.array([[0.5, 0.3, 0.2]]))
+    par, toks, dep = [-1, 0, 0], [0, 0, 1], [0, 1, 1]
+    got = _first_tokens(tgt, par, toks, dep, 3, 1, 1.0, rng, 20000, "topw")
+    counts = np.bincount(got[:, 0], minlength=3)
+    assert _chi2(counts, np.array([0.2, 0.2, 0.6])) < 13.8  # 2 dof, P = 0.001
+    # the i.i.d. rule on the same deterministic siblings never emits token 1
+    got = _first_tokens(tgt, par, toks, dep, 3, 1, 1.0, rng, 4000, "sampled", dft)
+    counts = np.bincount(got[:, 0], minlength=3)
+    assert counts[1] == 0 and abs(counts[0] / 4000 - 0.4) < 0.04
+
+
+@pytest.mark.parametrize("W,T", [(2, 1.0), (3, 0.7), (2, 1.75)])
+def test_stochastic_topw_tree_is_lossless_chi_square(W, T):
+    """A complete depth-2 tree whose siblings are the top-W tokens of each
+    depth's draft row (as the build step makes them).  The first emitted token
+    must follow softmax(root row / T); given that depth-1 node v was accepted,
+    the second emitted token must follow softmax(row v / T)."""
+    rng = np.random.default_rng(300 + 10 * W + int(T * 10))
+    V, N = 6, 2
+    draft = rng.standard_normal((N, V)) * 1.5
+    top = [list(np.lexsort((np.arange(V), -draft[d]))[:W]) for d in range(N)]
+    par, toks, dep = [-1], [0], [0]
+    for k in range(W):
+        par.append(0), toks.append(int(top[0][k])), dep.append(1)
+    for v in range(1, W + 1):
+        for k in range(W):
+            par.append(v), toks.append(int(top[1][k])), dep.append(2)
+    n = len(par)
+    tgt = rng.standard_normal((n, V)) * 1.5
+    trials = 30000
+    got = _first_tokens(tgt, par, toks, dep, n, N, T, rng, trials, "topw")
+    # 5 degrees of freedom: P(chi2 > 25.7) ~ 1e-4
+    assert _chi2(np.bincount(got[:, 0], minlength=V), O.softmax_t(tgt[0], T)) < 25.7
+    checked = 0
+    for v in range(1, W + 1):
+        sel = got[:, 2] == v
+        if sel.sum() < 1500:
+            continue
+        checked += 1
+        c2 = _chi2(np.bincount(got[sel, 1], minlength=V), O.softmax_t(tgt[v], T))
+        assert c2 < 25.7, (v, c2)
+    assert checked >= 1
+
+
 @pytest.mark.parametrize("k,T", [(1, 1.0), (3, 1.0), (4, 0.7)])
-def test_stochastic_is_lossless_chi_square(k, T):
-    """With k candidates drawn i.i.d. from the draft distribution q, the first
-    token the step emits (the accepted child's, else the bonus) must follow
-    the target distribution p exactly: a chi-square test over many trials."""
+def test_stochastic_sampled_is_lossless_chi_square(k, T):
+    """The i.i.d. proposal mode: with k candidates drawn i.i.d. from the draft
+    distribution q, the first token the step emits (the accepted child's, else
+    the bonus) must follow the target distribution p exactly."""
     rng = np.random.default_rng(1000 + 10 * k)
     V = 6
     tgt = rng.standard_normal((k + 1, V)) * 1.5
@@ -187,7 +295,7 @@ def test_stochastic_is_lossless_chi_square(k, T):
         toks = [0] + [int(t) for t in rng.choice(V, size=k, p=q)]
         ua = rng.random(k + 1)
         L, nodes, bonus = O.accept_stochastic(tgt, dft, par, toks, dep, k + 1, 1, T, ua,
-                                              rng.random())
+                                              rng.random(), draft_mode="sampled")
         counts[toks[nodes[0]] if L else bonus] += 1
     expected = p * trials
     chi2 = float(((counts - expected) ** 2 / expected).sum())
@@ -195,7 +303,7 @@ def test_stochastic_is_lossless_chi_square(k, T):
     assert chi2 < 22.1, (chi2, counts, expected)
 
 
-def test_stochastic_deterministic_draft_equal_to_target_accepts():
+def test_stochastic_sampled_draft_equal_to_target_accepts():
     """q == p: every drafted token passes (u * q(x) < p(x) for u < 1)."""
     rng = np.random.default_rng(5)
     V, n = 20, 12
@@ -206,7 +314,7 @@ def test_stochastic_deterministic_draft_equal_to_target_accepts():
     X = np.tile(X[0], (n, 1))
     tok = [0] + [int(rng.integers(0, V)) for _ in range(1, n)]
     L, nodes, _ = O.accept_stochastic(X, Dl, par, tok, dep, n, max(dep) + 1, 1.0,
-                                      rng.random(n) * 0.999, 0.5)
+                                      rng.random(n) * 0.999, 0.5, draft_mode="sampled")
     # the first child of every accepted node is accepted: the path follows first children
     u, expect = 0, []
     while True:
@@ -216,6 +324,35 @@ def test_stochastic_deterministic_draft_equal_to_target_accepts():
         u = kids[0]
         expect.append(u)
     assert nodes[:L].tolist() == expect
+
+
+def test_stochastic_topw_certain_token_is_accepted():
+    """A target row that puts all its mass on one token: the sibling holding
+    it is accepted whatever its uniform (u < 1 = p(x)); earlier siblings with
+    zero mass are rejected without changing p."""
+    V = 5
+    X = np.full((4, V), -np.inf)
+    X[:, 3] = 0.0
+    par, tok, dep = [-1, 0, 0, 0], [0, 1, 3, 4], [0, 1, 1, 1]
+    for u in (0.0, 0.5, 0.999):
+        L, nodes, bonus = O.accept_stochastic(X, None, par, tok, dep, 4, 1, 1.0,
+                                              np.array([0.0, u, u, u]), 0.5)
+        assert (L, nodes.tolist(), bonus) == (1, [2], 3)
+
+
+def test_stochastic_topw_duplicate_siblings():
+    """A caller tree with the same token on two siblings: the second try sees
+    p(x) = 0 after the first rejection and is rejected without changing p."""
+    X = np.log(np.array([[0.5, 0.3, 0.2]] * 4))
+    par, tok, dep = [-1, 0, 0, 0], [0, 1, 1, 0], [0, 1, 1, 1]
+    # 1st sibling (token 1) rejected: p = [5/7, 0, 2/7]; 2nd (token 1 again)
+    # rejected; 3rd (token 0): accepted iff u < 5/7
+    L, nodes, _ = O.accept_stochastic(X, None, par, tok, dep, 4, 1, 1.0,
+                                      np.array([0.0, 0.5, 0.0, 0.7]), 0.5)
+    assert (L, nodes.tolist()) == (1, [3])
+    L, nodes, bonus = O.accept_stochastic(X, None, par, tok, dep, 4, 1, 1.0,
+                                          np.array([0.0, 0.5, 0.0, 0.72]), 0.5)
+    assert (L, bonus) == (0, 2)  # p = [0, 0, 1]
 
 
 # ------------------------------------------------------- build-mode variants
