@@ -312,18 +312,23 @@ def time_next_rows(B, w, x, tree, d_draft, d_target, d_k, d_v, d_prefix, d_table
     par, tok, dep, nn = tree["parent"], tree["token"], tree["depth"], tree["n_nodes"]
     out = {}
     # margin acceptance: one pass over the target rows, like the greedy rule
-    us = timed(lambda: B.jt_accept_margin(d_target, w.depth_n, par, tok, dep, nn,
-                                          B.margin_from_ratio(0.5), err=err, workspace=ws_acc))
+    us = timed(lambda: B.jt_accept_margin(d_target, w.depth_n, par, tok, dep, nn, 0.5, 1.0,
+                                          err=err, workspace=ws_acc))
     tb = b * T * w.vocab * 4
     out["accept_margin"] = {"us": us, "target_bytes": tb, "gbps": tb / us / 1e3,
                             "hbm_frac": tb / us / 1e3 / PEAK_HBM_GBPS}
-    # stochastic verification at T = 1 with seeded uniforms (mostly rejections
-    # on these independent target rows: up to W residual passes per sequence)
+    # stochastic verification at T = 1 with seeded uniforms, on the build's
+    # top-W trees (point-mass proposals; mostly rejections on these
+    # independent target rows), and the i.i.d.-proposal rule for comparison
+    # (up to W residual passes per sequence)
     g = torch.Generator().manual_seed(17)
     ua = torch.rand((b, T), generator=g).to(dev)
     usamp = torch.rand((b,), generator=g).to(dev)
     out["accept_stochastic_us"] = timed(lambda: B.jt_accept_stochastic(
-        d_target, d_draft, par, tok, dep, nn, 1.0, ua, usamp, err=err))
+        d_target, w.depth_n, par, tok, dep, nn, 1.0, ua, usamp, err=err))
+    out["accept_stochastic_sampled_us"] = timed(lambda: B.jt_accept_stochastic(
+        d_target, w.depth_n, par, tok, dep, nn, 1.0, ua, usamp, draft_logits=d_draft,
+        draft_mode="sampled", err=err))
     # KV commit of each tree's deepest path (prefix_len restored before each call)
     depth_h, par_h = dep.cpu().numpy(), par.cpu().numpy()
     anodes = np.full((b, w.depth_n), -1, dtype=np.int32)

@@ -10,6 +10,7 @@
  *   jt_accept_margin   acceptance under a probability-ratio margin
  *   jt_commit_kv       move the accepted path's K/V next to the prefix
  *   jt_accept_stochastic  lossless verification at temperature T > 0
+ *                      (top-W siblings, or children sampled from the draft)
  *   jt_build_tree_variant  tree build under the alternative expansions and
  *                      priorities (node-block, entropy / mixed)
  *
@@ -60,6 +61,12 @@ typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
 
 /* Tree expansion of jt_build_tree_variant. */
 typedef enum { JT_EXPAND_CANDIDATE = 0, JT_EXPAND_NODE_BLOCK = 1 } jt_expand;
+
+/* How the drafted tokens of a tree were proposed (jt_accept_stochastic). */
+typedef enum {
+  JT_DRAFT_TOPW = 0,    /* siblings are distinct chosen tokens (jt_build_tree's top-W) */
+  JT_DRAFT_SAMPLED = 1  /* every child drawn i.i.d. from softmax(draft row / T)        */
+} jt_draft_mode;
 
 /* Device error bits (OR-ed into *err). */
 #define JT_DERR_BAD_LOGIT 1   /* NaN or +inf logit, or a draft row without a finite entry */
@@ -277,23 +284,27 @@ jt_status jt_accept(const void* target_logits, jt_dtype dt, int batch, int max_n
  * reaches a threshold theta, even when it is not the top-1 token (the page's
  * example keeps a token at 0.30 against a top-1 at 0.35 with theta = 0.8).
  * With p = softmax(L / T) that ratio is exp((L[x] - max L) / T), so the rule is
- * L[x] - max L >= logit_margin with logit_margin = T * ln(theta).
+ * L[x] - max L >= T * ln(theta); the library forms that logit margin on the
+ * host in fp64.
  *
  * Same arguments, outputs and walk as jt_accept, except the per-node test:
  * node v >= 1 is accepted iff its parent is accepted and
- *   (double)L[parent(v)][token[v]] - (double)max_x L[parent(v)][x] >= logit_margin
+ *   (double)L[parent(v)][token[v]] - (double)max_x L[parent(v)][x]
+ *       >= temperature * log(theta)
  * evaluated in fp64 on the stored logit values.  Several siblings may pass;
  * the path ends at the deepest accepted node (lowest index among equals) and
  * bonus_token is the argmax (lowest id) of that node's row.
- *   logit_margin  finite and <= 0 (0 keeps only tokens tied with the maximum).
- *   err           as jt_accept, plus JT_DERR_BAD_TOKEN (a token id outside
- *                 [0, vocab): that sequence's outputs are then zero / -1).
+ *   theta        in (0, 1] (1 keeps only tokens tied with the maximum).
+ *   temperature  > 0 and finite.
+ *   err          as jt_accept, plus JT_DERR_BAD_TOKEN (a token id outside
+ *                [0, vocab): that sequence's outputs are then zero / -1).
  * ---------------------------------------------------------------------- */
 jt_status jt_accept_margin(const void* target_logits, jt_dtype dt, int batch, int max_nodes,
                            int vocab, int depth_n, const int32_t* parent, const int32_t* token,
-                           const int32_t* depth, const int32_t* n_nodes, double logit_margin,
-                           int32_t* accept_len, int32_t* accept_nodes, int32_t* bonus_token,
-                           int32_t* err, void* workspace, size_t workspace_bytes, void* stream);
+                           const int32_t* depth, const int32_t* n_nodes, double theta,
+                           double temperature, int32_t* accept_len, int32_t* accept_nodes,
+                           int32_t* bonus_token, int32_t* err, void* workspace,
+                           size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------
  * jt_commit_kv -- commit the accepted path to the KV cache.
@@ -338,17 +349,32 @@ jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int n
  * strict token-matching rule): with draft distribution q and target
  * distribution p, a drafted token x is accepted with probability
  * min(1, p(x) / q(x)); on rejection the next token is drawn from
- * norm(max(0, p - q)), which leaves the output distributed as the target's.
+ * norm(max(0, p - q)), which leaves the output distributed as the target's
+ * provided x was proposed from q.  The proposal is named by draft_mode:
  *
- * Tree walk fixed here (the pages state the rule for one token):
- *  - p at node u = softmax(target row u / T); q of a depth-d child =
- *    softmax(draft row d / T) (the drafter's distributions are per depth).
+ *  JT_DRAFT_TOPW     the siblings are chosen tokens, as jt_build_tree makes
+ *                    them (the top-W draft tokens of each depth: JetSpec news
+ *                    piece, tree-construction paragraph; explainer section
+ *                    五).  Each sibling's proposal is the point mass on its
+ *                    token, so x is accepted with probability p(x) and a
+ *                    rejection removes x from p and renormalises.  The output
+ *                    follows the target distribution for any fixed tree.
+ *                    draft_logits is not read (may be NULL).
+ *  JT_DRAFT_SAMPLED  every child of a node was drawn independently from
+ *                    q = softmax(draft row of its depth / T): x is accepted
+ *                    iff u * q(x) < p(x) and a rejection sets
+ *                    p = norm(max(0, p - q)) with the same q for the next
+ *                    sibling.  Lossless only under that sampling assumption;
+ *                    on jt_build_tree's deterministic siblings it is NOT.
+ *
+ * Tree walk (the pages state the rule for one token):
+ *  - p at node u = softmax(target row u / T).
  *  - Starting at the root, the current node's children are tried in node-index
- *    order: child v (token x) is accepted iff u_accept[v] * q(x) < p(x) with p
- *    the current distribution; a rejection sets p = norm(max(0, p - q)) and
- *    the next child is tried; if that residual is all zero the remaining
- *    children are skipped and p stays as it was.  An accepted child becomes
- *    the current node.
+ *    order: child v (token x) is accepted iff u_accept[v] < p(x) (TOPW) or
+ *    u_accept[v] * q(x) < p(x) (SAMPLED), p being the current distribution;
+ *    a rejection replaces p by its residual and the next child is tried; if
+ *    that residual has no mass the remaining children are skipped and p stays
+ *    as it was.  An accepted child becomes the current node.
  *  - When no child is accepted the walk stops; bonus_token is the smallest
  *    y with sum_{i <= y} p(i) > u_sample * sum_i p(i) (index order).
  * Arithmetic: fp64 on the stored logit values (exp of the device math
@@ -356,7 +382,8 @@ jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int n
  * move decisions whose margin is at the rounding level (~1e-13 relative).
  *
  *   target_logits [batch, max_nodes, vocab]  dt; rows >= n_nodes not read.
- *   draft_logits  [batch, depth_n, vocab]    dt (row d-1 = depth d).
+ *   draft_logits  [batch, depth_n, vocab]    dt (row d-1 = depth d); SAMPLED
+ *                 only.
  *   parent, token, depth, n_nodes   as jt_accept.
  *   temperature   > 0 and finite.
  *   u_accept  [batch, max_nodes] f32: uniform in [0, 1) per node (entry 0 and
@@ -369,18 +396,20 @@ jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int n
  *             are then zero / -1).
  *   workspace  jt_accept_stochastic_workspace(batch, vocab) bytes (2 * vocab
  *             doubles per sequence: the exponentials of the current target
- *             row and of the children's draft row, reused by every pass; then
- *             16 bytes per 4096-entry chunk of the root's target row and the
- *             depth-1 draft row, whose statistics are computed up front).
+ *             row and, SAMPLED, of the children's draft row; then 20 bytes per
+ *             4096-entry chunk of the root's target row and the depth-1 draft
+ *             row, whose statistics are computed up front).  TOPW writes
+ *             zeros into the cached target row for rejected tokens.
  * Limits: batch >= 0, 1 <= max_nodes <= 1024, vocab >= 1, 1 <= depth_n <= 64.
- * Two short pre-pass kernels over every sequence's first two rows, then one
+ * Two short pre-pass kernels over every sequence's first rows, then one
  * workgroup per sequence for the walk.
  * ---------------------------------------------------------------------- */
 size_t jt_accept_stochastic_workspace(int batch, int vocab);
 jt_status jt_accept_stochastic(const void* target_logits, const void* draft_logits, jt_dtype dt,
                                int batch, int max_nodes, int vocab, int depth_n,
                                const int32_t* parent, const int32_t* token, const int32_t* depth,
-                               const int32_t* n_nodes, float temperature, const float* u_accept,
+                               const int32_t* n_nodes, float temperature,
+                               jt_draft_mode draft_mode, const float* u_accept,
                                const float* u_sample, int32_t* accept_len, int32_t* accept_nodes,
                                int32_t* bonus_token, int32_t* err, void* workspace,
                                size_t workspace_bytes, void* stream);

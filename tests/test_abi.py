@@ -130,12 +130,15 @@ def test_accept_margin_validation(lib):
     f = lib.jt_accept_margin
     p = ctypes.c_void_p(1)
 
-    def call(margin=-0.5, dt=0, b=1, T=17, V=100, N=4, ws=0):
-        return f(p, dt, b, T, V, N, p, p, p, p, margin, p, p, p, None, p, ws, None)
+    def call(theta=0.5, temp=1.0, dt=0, b=1, T=17, V=100, N=4, ws=0):
+        return f(p, dt, b, T, V, N, p, p, p, p, theta, temp, p, p, p, None, p, ws, None)
 
-    assert call(margin=0.1) == B.JT_ERR_INVALID_ARG           # a ratio above 1
-    assert call(margin=float("nan")) == B.JT_ERR_INVALID_ARG
-    assert call(margin=float("-inf")) == B.JT_ERR_INVALID_ARG
+    assert call(theta=1.1) == B.JT_ERR_INVALID_ARG            # a ratio above 1
+    assert call(theta=0.0) == B.JT_ERR_INVALID_ARG
+    assert call(theta=float("nan")) == B.JT_ERR_INVALID_ARG
+    assert call(temp=0.0) == B.JT_ERR_INVALID_ARG
+    assert call(temp=float("inf")) == B.JT_ERR_INVALID_ARG
+    assert call(temp=float("nan")) == B.JT_ERR_INVALID_ARG
     assert call(N=0) == B.JT_ERR_INVALID_ARG
     assert call(T=1025) == B.JT_ERR_UNSUPPORTED
     assert call(ws=0) == B.JT_ERR_WORKSPACE
@@ -163,11 +166,13 @@ def test_accept_stochastic_validation(lib):
 
     need = lib.jt_accept_stochastic_workspace(1, 100)
     # 2 x 100 doubles (et, ed) padded to 256 bytes, then one 4096-entry chunk
-    # for each of the two pre-pass rows: sum (8) + max (4) + flag (4) bytes
-    assert need == 1792 + 2 * 16
+    # for each of the two pre-pass rows: sum (8) + max (4) + flag (4) +
+    # positive count (4) bytes
+    assert need == 1792 + 2 * 20
 
-    def call(temp=0.7, dt=1, b=1, T=17, V=100, N=4, ua=p, ws=need):
-        return f(p, p, dt, b, T, V, N, p, p, p, p, temp, ua, p, p, p, p, None, p, ws, None)
+    def call(temp=0.7, dt=1, b=1, T=17, V=100, N=4, ua=p, ws=need, mode=0, draft=p):
+        return f(p, draft, dt, b, T, V, N, p, p, p, p, temp, mode, ua, p, p, p, p, None, p, ws,
+                 None)
 
     assert call(temp=0.0) == B.JT_ERR_INVALID_ARG
     assert call(temp=-1.0) == B.JT_ERR_INVALID_ARG
@@ -178,6 +183,8 @@ def test_accept_stochastic_validation(lib):
     assert call(T=1025) == B.JT_ERR_UNSUPPORTED
     assert call(ua=None) == B.JT_ERR_INVALID_ARG
     assert call(ws=need - 1) == B.JT_ERR_WORKSPACE
+    assert call(mode=2) == B.JT_ERR_INVALID_ARG
+    assert call(mode=1, draft=None) == B.JT_ERR_INVALID_ARG   # sampled children need the draft
     assert call(b=0) == B.JT_OK
 
 

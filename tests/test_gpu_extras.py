@@ -36,27 +36,32 @@ def _pad(rows, T, fill=-1):
     return [list(r) + [fill] * (T - len(r)) for r in rows]
 
 
-def _gpu_margin(X, N, parents, tokens, depths, ns, margin):
+def _gpu_margin(X, N, parents, tokens, depths, ns, theta, temp=1.0):
     d = dev()
     err = torch.zeros(1, dtype=torch.int32, device=d)
     i32 = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.int32).to(d)
     alen, anodes, bonus = B.jt_accept_margin(X.to(d), N, i32(parents), i32(tokens), i32(depths),
-                                             i32(ns), margin, err=err)
+                                             i32(ns), theta, temp, err=err)
     torch.cuda.synchronize()
     return to_np(alen), to_np(anodes), to_np(bonus), int(err.item())
 
 
 # ------------------------------------------------------------ margin accept
 
-def test_margin_page_example_on_gpu():
+@pytest.mark.parametrize("temp", [1.0, 0.5, 1.75])
+def test_margin_page_example_on_gpu(temp):
+    """The page's probabilities as logits T * ln(p): softmax(L / T) gives the
+    page's probabilities back, so every temperature must keep the page's
+    decisions (theta = 0.8 keeps 0.30 against 0.35, theta = 0.9 does not)."""
     g = json.load(open(os.path.join(GOLDEN, "margin_example.json")))
-    X = torch.from_numpy(np.log(np.array(g["target_probs"], dtype=np.float64)).astype(np.float32))
+    X = torch.from_numpy(
+        (temp * np.log(np.array(g["target_probs"], dtype=np.float64))).astype(np.float32))
     for c in g["cases"]:
-        m = B.margin_from_ratio(c["theta"])
         alen, anodes, bonus, err = _gpu_margin(X[None], 1, [g["parent"]], [g["token"]],
-                                               [g["depth"]], [2], m)
+                                               [g["depth"]], [2], c["theta"], temp)
         assert err == 0
         # the float32 logits must give the same decisions as the page's ratios
+        m = O.margin_from_ratio(c["theta"], temp)
         L, nodes, bb = O.accept_margin(X.numpy(), g["parent"], g["token"], g["depth"], 2, 1, m)
         assert (L, nodes.tolist(), bb) == (c["accept_len"], c["accept_nodes"], c["bonus"])
         assert (int(alen[0]), anodes[0].tolist(), int(bonus[0])) == (L, nodes.tolist(), bb)
@@ -78,9 +83,11 @@ def test_margin_small_random_trees(seed, dtype):
     X = torch.from_numpy(np.round(rng.standard_normal((b, T, V)) * 2, 1).astype(np.float32))
     if dtype == "bf16":
         X = X.to(torch.bfloat16)
-    margin = -float(rng.uniform(0.0, 2.5))
+    theta = float(np.exp(-rng.uniform(0.0, 2.5)))
+    temp = (1.0, 0.6, 1.4)[seed % 3]
+    margin = O.margin_from_ratio(theta, temp)
     alen, anodes, bonus, err = _gpu_margin(X, N, _pad(pars, T), _pad(toks, T, 0), _pad(deps, T),
-                                           ns, margin)
+                                           ns, theta, temp)
     assert err == 0
     Xf = X.float().numpy()
     for s in range(b):
@@ -109,8 +116,9 @@ def test_margin_workload_planted(oracle_trees_extras):
         tgt[p, int(t["token"][v])] = tgt[p].max() - 0.5
     par, tok, dep = t["parent"], t["token"], t["depth"]
     for theta in (0.9, 0.5, 0.3):
-        m = B.margin_from_ratio(theta)
-        alen, anodes, bonus, err = _gpu_margin(tgt[None], w.depth_n, [par], [tok], [dep], [n], m)
+        m = O.margin_from_ratio(theta)
+        alen, anodes, bonus, err = _gpu_margin(tgt[None], w.depth_n, [par], [tok], [dep], [n],
+                                               theta)
         assert err == 0
         L, nodes, bb = O.accept_margin(tgt.numpy(), par, tok, dep, n, w.depth_n, m)
         assert (int(alen[0]), int(bonus[0])) == (L, bb), theta
@@ -120,7 +128,8 @@ def test_margin_workload_planted(oracle_trees_extras):
 
 def test_margin_rejects_bad_token():
     X = torch.zeros((1, 3, 8))
-    alen, anodes, bonus, err = _gpu_margin(X, 2, [[-1, 0, 1]], [[0, 9, 1]], [[0, 1, 2]], [3], -1.0)
+    alen, anodes, bonus, err = _gpu_margin(X, 2, [[-1, 0, 1]], [[0, 9, 1]], [[0, 1, 2]], [3],
+                                           float(np.exp(-1.0)))
     assert err & B.DERR_BAD_TOKEN
     assert int(alen[0]) == 0 and (anodes[0] == -1).all()
 
@@ -284,27 +293,32 @@ def test_commit_then_decode_matches_tree_attention():
 _REL_FLIP = 1e-9  # decisions closer than this to flipping may differ by summation order
 
 
-def _gpu_stochastic(X, Dl, parents, tokens, depths, ns, temp, ua, us):
+def _gpu_stochastic(X, Dl, parents, tokens, depths, ns, temp, ua, us, mode="sampled", N=None):
     d = dev()
     err = torch.zeros(1, dtype=torch.int32, device=d)
     i32 = lambda a: torch.as_tensor(np.asarray(a), dtype=torch.int32).to(d)
     f32 = lambda a: torch.as_tensor(np.asarray(a, dtype=np.float32)).to(d)
+    if N is None:
+        N = Dl.shape[1]
     alen, anodes, bonus = B.jt_accept_stochastic(
-        X.to(d).contiguous(), Dl.to(d).contiguous(), i32(parents), i32(tokens), i32(depths),
-        i32(ns), temp, f32(ua), f32(us), err=err)
+        X.to(d).contiguous(), N, i32(parents), i32(tokens), i32(depths), i32(ns), temp, f32(ua),
+        f32(us), draft_logits=None if Dl is None else Dl.to(d).contiguous(), draft_mode=mode,
+        err=err)
     torch.cuda.synchronize()
     return to_np(alen), to_np(anodes), to_np(bonus), int(err.item())
 
 
-def _compare_stochastic(Xf, Df, pars, toks, deps, ns, N, temp, ua, us, alen, anodes, bonus):
+def _compare_stochastic(Xf, Df, pars, toks, deps, ns, N, temp, ua, us, alen, anodes, bonus,
+                        mode="sampled"):
     """Exact agreement wherever no decision of the oracle's walk is within
     rounding of flipping; returns the number of sequences compared."""
     compared = 0
     for s in range(len(ns)):
         margins = []
-        L, nodes, bb = O.accept_stochastic(Xf[s], Df[s], pars[s], toks[s], deps[s], ns[s], N,
-                                           temp, np.asarray(ua[s], dtype=np.float32),
-                                           np.float32(us[s]), margins=margins)
+        L, nodes, bb = O.accept_stochastic(Xf[s], None if Df is None else Df[s], pars[s], toks[s],
+                                           deps[s], ns[s], N, temp,
+                                           np.asarray(ua[s], dtype=np.float32),
+                                           np.float32(us[s]), margins=margins, draft_mode=mode)
         if min(margins) < _REL_FLIP:
             continue
         compared += 1
@@ -313,7 +327,7 @@ def _compare_stochastic(Xf, Df, pars, toks, deps, ns, N, temp, ua, us, alen, ano
     return compared
 
 
-def test_stochastic_page_example_on_gpu():
+def test_stochastic_sampled_page_example_on_gpu():
     g = json.load(open(os.path.join(GOLDEN, "stochastic_example.json")))
     X = torch.from_numpy(np.log(np.array(g["target_probs"])).astype(np.float32))[None]
     Dl = torch.from_numpy(np.log(np.array(g["draft_probs"])).astype(np.float32))[None]
@@ -324,6 +338,154 @@ def test_stochastic_page_example_on_gpu():
         assert err == 0
         assert (int(alen[0]), anodes[0].tolist(), int(bonus[0])) == (
             c["accept_len"], c["accept_nodes"], c["bonus"]), c
+
+
+def test_stochastic_topw_page_example_on_gpu():
+    g = json.load(open(os.path.join(GOLDEN, "stochastic_topw_example.json")))
+    X = torch.from_numpy(np.log(np.array(g["target_probs"])).astype(np.float32))[None]
+    for c in g["cases"]:
+        alen, anodes, bonus, err = _gpu_stochastic(X, None, [g["parent"]], [g["token"]],
+                                                   [g["depth"]], [4], 1.0, [c["u_accept"]],
+                                                   [c["u_sample"]], mode="topw", N=g["n_depth"])
+        assert err == 0
+        assert (int(alen[0]), anodes[0].tolist(), int(bonus[0])) == (
+            c["accept_len"], c["accept_nodes"], c["bonus"]), c
+
+
+def _topw_case(rng, b, T, V, N, W, noise):
+    """Random trees whose siblings are the top-ranked tokens of their depth's
+    draft row (distinct, rank order = node order, as the build makes them);
+    target rows are the children's draft row plus noise, so the top tokens
+    are accepted often."""
+    Dl = rng.standard_normal((b, N, V)) * 2.0
+    X = rng.standard_normal((b, T, V)) * 2.0
+    pars, deps, toks, ns = [], [], [], []
+    for s in range(b):
+        order = [list(np.lexsort((np.arange(V), -Dl[s, d]))) for d in range(N)]
+        par, dep, tok, kids = [-1], [0], [0], [0]
+        n = int(rng.integers(1, T + 1))
+        while len(par) < n:
+            cand = [u for u in range(len(par)) if dep[u] < N and kids[u] < W]
+            if not cand:
+                break
+            u = int(rng.choice(cand))
+            par.append(u), dep.append(dep[u] + 1), tok.append(int(order[dep[u]][kids[u]]))
+            kids[u] += 1
+            kids.append(0)
+        pars.append(par), deps.append(dep), toks.append(tok), ns.append(len(par))
+        for u in range(len(par)):
+            if dep[u] < N:
+                X[s, u] = Dl[s, dep[u]] + noise * rng.standard_normal(V)
+    return X, Dl, pars, deps, toks, ns
+
+
+@pytest.mark.parametrize("seed,dtype,temp,V", [(0, "f32", 1.0, 40), (1, "bf16", 1.0, 40),
+                                               (2, "f32", 0.5, 40), (3, "bf16", 1.75, 40),
+                                               (4, "f32", 0.25, 37), (5, "bf16", 0.7, 37),
+                                               (6, "f32", 1.3, 42), (7, "bf16", 0.5, 42)])
+def test_stochastic_topw_small_random_trees(seed, dtype, temp, V):
+    rng = np.random.default_rng(900 + seed)
+    b, T, N, W = 16, 60, 12, 4
+    X, Dl, pars, deps, toks, ns = _topw_case(rng, b, T, V, N, W, noise=0.5)
+    ua = rng.random((b, T)).astype(np.float32)
+    us = rng.random(b).astype(np.float32)
+    Xt = torch.from_numpy(X.astype(np.float32))
+    if dtype == "bf16":
+        Xt = Xt.to(torch.bfloat16)
+    alen, anodes, bonus, err = _gpu_stochastic(Xt, None, _pad(pars, T), _pad(toks, T, 0),
+                                               _pad(deps, T), ns, temp, ua, us, mode="topw", N=N)
+    assert err == 0
+    n_cmp = _compare_stochastic(Xt.float().numpy(), None, pars, toks, deps, ns, N, temp, ua, us,
+                                alen, anodes, bonus, mode="topw")
+    assert n_cmp >= b - 1
+    assert (alen > 0).any()
+
+
+def test_stochastic_topw_edge_cases():
+    """A row whose mass sits on one token (its sibling is accepted whatever
+    the uniform, zero-mass siblings before it are rejected) and duplicate
+    sibling tokens (the repeat sees its mass already removed)."""
+    V = 8
+    X = np.full((2, 4, V), -np.inf, dtype=np.float32)
+    X[0, :, 3] = 0.0
+    X[1] = np.log(np.array([0.5, 0.3, 0.2, 1e-3, 1e-3, 1e-3, 1e-3, 1e-3], dtype=np.float32))
+    pars = [[-1, 0, 0, 0], [-1, 0, 0, 0]]
+    toks = [[0, 1, 3, 4], [0, 1, 1, 0]]
+    deps = [[0, 1, 1, 1], [0, 1, 1, 1]]
+    for ua_row in ([0.0, 0.999, 0.999, 0.999], [0.0, 0.5, 0.0, 0.7], [0.0, 0.5, 0.0, 0.72]):
+        ua = np.array([ua_row, ua_row], dtype=np.float32)
+        us = np.array([0.5, 0.3], dtype=np.float32)
+        alen, anodes, bonus, err = _gpu_stochastic(torch.from_numpy(X), None, pars, toks, deps,
+                                                   [4, 4], 1.0, ua, us, mode="topw", N=1)
+        assert err == 0
+        assert (int(alen[0]), int(anodes[0][0]), int(bonus[0])) == (1, 2, 3)
+        assert _compare_stochastic(X, None, pars, toks, deps, [4, 4], 1, 1.0, ua, us, alen,
+                                   anodes, bonus, mode="topw") == 2
+
+
+@pytest.mark.parametrize("W,temp", [(1, 1.0), (4, 0.7), (8, 1.4)])
+def test_stochastic_topw_gpu_output_follows_target_chi_square(W, temp):
+    """Losslessness on the device for the build's trees: 8192 sequences, each
+    a root whose W children are the top-W tokens of the draft row (chosen,
+    not sampled); the first emitted token must follow softmax(root row / T)."""
+    rng = np.random.default_rng(190 + W)
+    b, V = 8192, 10
+    root_row = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    drow = (rng.standard_normal(V) * 1.5).astype(np.float32)
+    X = torch.from_numpy(np.tile(root_row, (b, W + 1, 1)))
+    top = np.lexsort((np.arange(V), -drow))[:W]
+    toks = np.zeros((b, W + 1), dtype=np.int64)
+    toks[:, 1:] = top
+    par = [[-1] + [0] * W] * b
+    dep = [[0] + [1] * W] * b
+    ua = rng.random((b, W + 1)).astype(np.float32)
+    us = rng.random(b).astype(np.float32)
+    alen, anodes, bonus, err = _gpu_stochastic(X, None, par, toks, dep, [W + 1] * b, temp, ua, us,
+                                               mode="topw", N=1)
+    assert err == 0
+    first = np.where(alen > 0, toks[np.arange(b), np.maximum(anodes[:, 0], 0)], bonus)
+    counts = np.bincount(first, minlength=V)
+    expected = O.softmax_t(root_row, temp) * b
+    chi2 = float(((counts - expected) ** 2 / expected).sum())
+    assert chi2 < 29.7, (chi2, counts, expected)  # 9 degrees of freedom, P = 0.0005
+
+
+def test_stochastic_topw_gpu_two_levels_chi_square():
+    """A complete depth-2 top-3 tree over 8 tokens, 8192 sequences: the
+    second emitted token, given that depth-1 node v was accepted, must follow
+    softmax(row v)."""
+    rng = np.random.default_rng(4711)
+    b, V, W = 8192, 8, 3
+    draft = rng.standard_normal((2, V)) * 1.5
+    top = [np.lexsort((np.arange(V), -draft[d]))[:W] for d in range(2)]
+    par, tok, dep = [-1], [0], [0]
+    for k in range(W):
+        par.append(0), tok.append(int(top[0][k])), dep.append(1)
+    for v in range(1, W + 1):
+        for k in range(W):
+            par.append(v), tok.append(int(top[1][k])), dep.append(2)
+    n = len(par)
+    rows = (rng.standard_normal((n, V)) * 1.5).astype(np.float32)
+    rows[0, top[0]] += 1.5  # accept often at depth 1
+    X = torch.from_numpy(np.tile(rows, (b, 1, 1)))
+    ua = rng.random((b, n)).astype(np.float32)
+    us = rng.random(b).astype(np.float32)
+    alen, anodes, bonus, err = _gpu_stochastic(X, None, [par] * b, [tok] * b, [dep] * b, [n] * b,
+                                               1.0, ua, us, mode="topw", N=2)
+    assert err == 0
+    tk = np.array(tok)
+    second = np.where(alen > 1, tk[np.maximum(anodes[:, 1], 0)], bonus)
+    checked = 0
+    for v in range(1, W + 1):
+        sel = (alen > 0) & (anodes[:, 0] == v)
+        if sel.sum() < 1000:
+            continue
+        checked += 1
+        counts = np.bincount(second[sel], minlength=V)
+        expected = O.softmax_t(rows[v], 1.0) * sel.sum()
+        chi2 = float(((counts - expected) ** 2 / expected).sum())
+        assert chi2 < 26.1, (v, chi2, counts, expected)  # 7 dof, P = 0.0005
+    assert checked >= 2
 
 
 def _correlated_case(rng, b, T, V, N, noise):
@@ -360,7 +522,7 @@ def _correlated_case(rng, b, T, V, N, noise):
                                                (4, "f32", 0.25, 40), (5, "bf16", 0.5, 40),
                                                (6, "f32", 1.0, 37), (7, "bf16", 0.7, 37),
                                                (8, "f32", 1.0, 42), (9, "bf16", 1.3, 42)])
-def test_stochastic_small_random_trees(seed, dtype, temp, V):
+def test_stochastic_sampled_small_random_trees(seed, dtype, temp, V):
     rng = np.random.default_rng(700 + seed)
     b, T, N = 16, 60, 12
     X, Dl, pars, deps, toks, ns = _correlated_case(rng, b, T, V, N, noise=0.6)
@@ -379,7 +541,7 @@ def test_stochastic_small_random_trees(seed, dtype, temp, V):
     assert (alen > 0).any() and (alen < np.array([max(d) for d in deps])).any()
 
 
-def test_stochastic_draft_equal_to_target_follows_first_children():
+def test_stochastic_sampled_draft_equal_to_target_follows_first_children():
     rng = np.random.default_rng(31)
     V, n, N = 64, 40, 40
     par, dep = _tree(rng, n)
@@ -391,7 +553,7 @@ def test_stochastic_draft_equal_to_target_follows_first_children():
     alen, anodes, bonus, err = _gpu_stochastic(X, Dl, [par], [tok], [dep], [n], 1.0, ua, [0.5])
     assert err == 0
     L, nodes, bb = O.accept_stochastic(X[0].numpy(), Dl[0].numpy(), par, tok, dep, n, N, 1.0,
-                                       ua[0], np.float32(0.5))
+                                       ua[0], np.float32(0.5), draft_mode="sampled")
     assert (int(alen[0]), anodes[0].tolist(), int(bonus[0])) == (L, nodes.tolist(), bb)
     u, first_children = 0, []
     while any(par[v] == u for v in range(n)):
@@ -400,7 +562,8 @@ def test_stochastic_draft_equal_to_target_follows_first_children():
     assert anodes[0][:L].tolist() == first_children
 
 
-def test_stochastic_workload_tree(oracle_trees_extras):
+@pytest.mark.parametrize("mode", ["topw", "sampled"])
+def test_stochastic_workload_tree(oracle_trees_extras, mode):
     """The B=256 tree over the 151936-token vocabulary (two sequences); target
     rows are the children's draft row plus noise."""
     name = "qwen3_8b_b256"
@@ -429,20 +592,22 @@ def test_stochastic_workload_tree(oracle_trees_extras):
     for dtype in ("f32", "bf16"):
         Xt, Dt = (X, draft) if dtype == "f32" else (X.to(torch.bfloat16),
                                                     draft.to(torch.bfloat16))
-        _say(f"stochastic workload {name} {dtype}")
-        alen, anodes, bonus, err = _gpu_stochastic(Xt, Dt, _pad(pars, T), _pad(toks, T, 0),
-                                                   _pad(deps, T), ns, 1.0, ua, us)
+        _say(f"stochastic workload {name} {dtype} {mode}")
+        alen, anodes, bonus, err = _gpu_stochastic(Xt, Dt if mode == "sampled" else None,
+                                                   _pad(pars, T), _pad(toks, T, 0),
+                                                   _pad(deps, T), ns, 1.0, ua, us, mode=mode, N=N)
         assert err == 0
-        n_cmp = _compare_stochastic(Xt.float().numpy(), Dt.float().numpy(), pars, toks, deps, ns,
-                                    N, 1.0, ua, us, alen, anodes, bonus)
+        n_cmp = _compare_stochastic(Xt.float().numpy(),
+                                    Dt.float().numpy() if mode == "sampled" else None, pars, toks,
+                                    deps, ns, N, 1.0, ua, us, alen, anodes, bonus, mode=mode)
         assert n_cmp == 2
 
 
 @pytest.mark.parametrize("k,temp", [(1, 1.0), (4, 0.7)])
-def test_stochastic_gpu_output_follows_target_chi_square(k, temp):
-    """Losslessness on the device: 8192 sequences, each a root with k children
-    whose tokens are drawn from q; the first emitted token (accepted child's,
-    else the bonus) must follow p = softmax(root row / T)."""
+def test_stochastic_sampled_gpu_output_follows_target_chi_square(k, temp):
+    """Losslessness on the device, i.i.d. proposals: 8192 sequences, each a
+    root with k children whose tokens are drawn from q; the first emitted
+    token (accepted child's, else the bonus) must follow p = softmax(root row / T)."""
     rng = np.random.default_rng(90 + k)
     b, V = 8192, 8
     root_row = (rng.standard_normal(V) * 1.5).astype(np.float32)
@@ -456,7 +621,8 @@ def test_stochastic_gpu_output_follows_target_chi_square(k, temp):
     dep = [[0] + [1] * k] * b
     ua = rng.random((b, k + 1)).astype(np.float32)
     us = rng.random(b).astype(np.float32)
-    alen, anodes, bonus, err = _gpu_stochastic(X, Dl, par, toks, dep, [k + 1] * b, temp, ua, us)
+    alen, anodes, bonus, err = _gpu_stochastic(X, Dl, par, toks, dep, [k + 1] * b, temp, ua, us,
+                                               mode="sampled")
     assert err == 0
     first = np.where(alen > 0, toks[np.arange(b), np.maximum(anodes[:, 0], 0)], bonus)
     counts = np.bincount(first, minlength=V)
@@ -465,17 +631,20 @@ def test_stochastic_gpu_output_follows_target_chi_square(k, temp):
     assert chi2 < 26.1, (chi2, counts, expected)  # 7 degrees of freedom, P = 0.0005
 
 
-def test_stochastic_rejects_bad_uniform():
+@pytest.mark.parametrize("mode", ["topw", "sampled"])
+def test_stochastic_rejects_bad_uniform(mode):
     X = torch.zeros((2, 2, 8))
     Dl = torch.zeros((2, 1, 8))
     alen, anodes, bonus, err = _gpu_stochastic(X, Dl, [[-1, 0]] * 2, [[0, 3]] * 2, [[0, 1]] * 2,
-                                               [2, 2], 1.0, [[0.0, 0.5], [0.0, 0.5]], [0.3, 1.0])
+                                               [2, 2], 1.0, [[0.0, 0.5], [0.0, 0.5]], [0.3, 1.0],
+                                               mode=mode)
     assert err & B.DERR_BAD_UNIFORM
     assert int(alen[1]) == 0 and int(bonus[1]) == -1
     assert int(bonus[0]) >= 0
 
 
-def test_stochastic_max_nodes():
+@pytest.mark.parametrize("mode", ["topw", "sampled"])
+def test_stochastic_max_nodes(mode):
     """A 1024-node tree (the largest the call takes), correlated targets."""
     rng = np.random.default_rng(4242)
     b, T, V, N = 2, 1024, 48, 64
@@ -498,10 +667,11 @@ def test_stochastic_max_nodes():
     us = rng.random(b).astype(np.float32)
     Xt = torch.from_numpy(X.astype(np.float32))
     Dt = torch.from_numpy(Dl.astype(np.float32))
-    alen, anodes, bonus, err = _gpu_stochastic(Xt, Dt, pars, toks, deps, ns, 1.0, ua, us)
+    alen, anodes, bonus, err = _gpu_stochastic(Xt, Dt, pars, toks, deps, ns, 1.0, ua, us,
+                                               mode=mode)
     assert err == 0
-    assert _compare_stochastic(Xt.numpy(), Dt.numpy(), pars, toks, deps, ns, N, 1.0, ua, us,
-                               alen, anodes, bonus) == b
+    assert _compare_stochastic(Xt.numpy(), Dt.numpy() if mode == "sampled" else None, pars, toks,
+                               deps, ns, N, 1.0, ua, us, alen, anodes, bonus, mode=mode) == b
 
 
 def test_margin_max_nodes():
@@ -513,8 +683,9 @@ def test_margin_max_nodes():
             break
     tok = [0] + [int(t) for t in rng.integers(0, V, T - 1)]
     X = torch.from_numpy(np.round(rng.standard_normal((1, T, V)) * 2, 1).astype(np.float32))
-    alen, anodes, bonus, err = _gpu_margin(X, N, [p], [tok], [dd], [T], -1.0)
+    theta = float(np.exp(-1.0))
+    alen, anodes, bonus, err = _gpu_margin(X, N, [p], [tok], [dd], [T], theta)
     assert err == 0
-    L, nodes, bb = O.accept_margin(X[0].numpy(), p, tok, dd, T, N, -1.0)
+    L, nodes, bb = O.accept_margin(X[0].numpy(), p, tok, dd, T, N, O.margin_from_ratio(theta))
     assert (int(alen[0]), int(bonus[0])) == (L, bb)
     assert np.array_equal(anodes[0], nodes)

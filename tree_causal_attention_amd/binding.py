@@ -19,6 +19,7 @@ LIB_PATH = os.path.join(HERE, "libjt.so")
 
 JT_F32, JT_BF16 = 0, 1
 JT_EXPAND_CANDIDATE, JT_EXPAND_NODE_BLOCK = 0, 1
+JT_DRAFT_TOPW, JT_DRAFT_SAMPLED = 0, 1
 JT_OK, JT_ERR_INVALID_ARG, JT_ERR_UNSUPPORTED, JT_ERR_WORKSPACE, JT_ERR_LAUNCH = range(5)
 DERR_BAD_LOGIT, DERR_BAD_PARENT, DERR_BAD_NNODES, DERR_BAD_PAGE, DERR_BAD_PREFIX, DERR_BAD_DEPTH = (
     1, 2, 4, 8, 16, 32)
@@ -44,13 +45,14 @@ SIGNATURES = {
     "jt_accept": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _c_size, _vp]),
     "jt_accept_margin": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
-                                  ctypes.c_double, _vp, _vp, _vp, _vp, _vp, _c_size, _vp]),
+                                  ctypes.c_double, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
+                                  _c_size, _vp]),
     "jt_commit_kv": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
                               _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "jt_accept_stochastic_workspace": (_c_size, [_c_int, _c_int]),
     "jt_accept_stochastic": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
-                                      _vp, _vp, _c_float, _vp, _vp, _vp, _vp, _vp, _vp, _vp, _c_size,
-                                      _vp]),
+                                      _vp, _vp, _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
+                                      _c_size, _vp]),
 }
 
 
@@ -176,8 +178,24 @@ def jt_tree_attention(q, k_pool, v_pool, n_nodes, prefix_len, page_table, num_pa
     for t, nm in ((q, "q"), (k_pool, "k_pool"), (v_pool, "v_pool"), (page_table, "page_table")):
         _cuda(t, nm)
     b, T, hq, D = q.shape
+    if k_pool.dim() != 4 or k_pool.shape != v_pool.shape or k_pool.shape[3] != D:
+        raise ValueError("k_pool and v_pool must both be [num_pages, Hkv, page_size, head_dim]")
+    if k_pool.dtype != q.dtype or v_pool.dtype != q.dtype:
+        raise TypeError("q, k_pool and v_pool must share a dtype")
     hkv, ps = k_pool.shape[1], k_pool.shape[2]
+    if page_table.dim() != 2 or page_table.shape[0] != b:
+        raise ValueError("page_table must be [batch, max_pages]")
     maxp = page_table.shape[1]
+    if not 1 <= int(num_pages) <= k_pool.shape[0]:
+        raise ValueError(f"num_pages={num_pages} outside [1, {k_pool.shape[0]}] (the pool's pages)")
+    for t, nm, shape in ((n_nodes, "n_nodes", (b,)), (prefix_len, "prefix_len", (b,)),
+                         (page_table, "page_table", None),
+                         (anc_mask, "anc_mask", (b, T, (T + 31) // 32))):
+        _cuda(t, nm)
+        if t.dtype != torch.int32 or t.device != q.device:
+            raise TypeError(f"{nm} must be an int32 tensor on {q.device}")
+        if shape is not None and tuple(t.shape) != shape:
+            raise ValueError(f"{nm} has shape {tuple(t.shape)}, expected {shape}")
     dt = _dtype_code(q)
     if out is None:
         out = torch.empty_like(q)
@@ -212,8 +230,9 @@ def jt_accept(target_logits, depth_n: int, parent, token, depth, n_nodes, err=No
 
 
 def jt_accept_margin(target_logits, depth_n: int, parent, token, depth, n_nodes,
-                     logit_margin: float, err=None, workspace=None):
-    """Margin acceptance; logit_margin = T ln(theta) (see margin_from_ratio).
+                     theta: float, temperature: float = 1.0, err=None, workspace=None):
+    """Margin acceptance: keep a token whose probability ratio to the top-1
+    token, under softmax(logits / temperature), reaches theta in (0, 1].
 
     Returns (accept_len [b], accept_nodes [b, depth_n], bonus_token [b]).
     """
@@ -228,15 +247,9 @@ def jt_accept_margin(target_logits, depth_n: int, parent, token, depth, n_nodes,
     ws = workspace if workspace is not None else _workspace(nbytes, dev)
     _check("jt_accept_margin", lib.jt_accept_margin(
         _ptr(target_logits), _dtype_code(target_logits), b, T, V, depth_n, _ptr(parent),
-        _ptr(token), _ptr(depth), _ptr(n_nodes), float(logit_margin), _ptr(alen), _ptr(anodes),
-        _ptr(bonus), _ptr(err), _ptr(ws), ws.numel(), _stream()))
+        _ptr(token), _ptr(depth), _ptr(n_nodes), float(theta), float(temperature), _ptr(alen),
+        _ptr(anodes), _ptr(bonus), _ptr(err), _ptr(ws), ws.numel(), _stream()))
     return alen, anodes, bonus
-
-
-def margin_from_ratio(theta: float, temperature: float = 1.0) -> float:
-    """logit_margin for a probability-ratio threshold theta in (0, 1] at temperature T."""
-    import math
-    return float(temperature) * math.log(float(theta))
 
 
 def jt_commit_kv(k_pool, v_pool, page_table, num_pages, n_nodes, max_nodes: int, accept_len,
@@ -255,25 +268,36 @@ def jt_commit_kv(k_pool, v_pool, page_table, num_pages, n_nodes, max_nodes: int,
         _ptr(accept_nodes), _ptr(prefix_len), _ptr(err), _stream()))
 
 
-def jt_accept_stochastic(target_logits, draft_logits, parent, token, depth, n_nodes,
-                         temperature: float, u_accept, u_sample, err=None, workspace=None):
+def jt_accept_stochastic(target_logits, depth_n: int, parent, token, depth, n_nodes,
+                         temperature: float, u_accept, u_sample, draft_logits=None,
+                         draft_mode: str = "topw", err=None, workspace=None):
     """Lossless verification at temperature T > 0 with caller-supplied uniforms.
 
+    draft_mode "topw": siblings are chosen tokens (jt_build_tree's trees);
+    draft_logits is not used.  "sampled": every child was drawn i.i.d. from
+    softmax(draft row / T); draft_logits [b, depth_n, V] is required.
     u_accept [b, max_nodes] f32, u_sample [b] f32, all in [0, 1).
     Returns (accept_len [b], accept_nodes [b, depth_n], bonus_token [b]).
     """
     lib = load()
-    for t, nm in ((target_logits, "target_logits"), (draft_logits, "draft_logits"),
-                  (u_accept, "u_accept"), (u_sample, "u_sample")):
+    modes = {"topw": JT_DRAFT_TOPW, "sampled": JT_DRAFT_SAMPLED}
+    if draft_mode not in modes:
+        raise ValueError(f"unknown draft mode {draft_mode!r}")
+    for t, nm in ((target_logits, "target_logits"), (u_accept, "u_accept"),
+                  (u_sample, "u_sample")):
         _cuda(t, nm)
-    if draft_logits.dtype != target_logits.dtype:
-        raise TypeError("target_logits and draft_logits must share a dtype")
+    b, T, V = target_logits.shape
+    if draft_mode == "sampled":
+        if draft_logits is None:
+            raise ValueError("draft_mode='sampled' needs draft_logits")
+        _cuda(draft_logits, "draft_logits")
+        if draft_logits.dtype != target_logits.dtype:
+            raise TypeError("target_logits and draft_logits must share a dtype")
+        if tuple(draft_logits.shape) != (b, depth_n, V):
+            raise ValueError("draft_logits must be [batch, depth_n, vocab]")
     if u_accept.dtype != torch.float32 or u_sample.dtype != torch.float32:
         raise TypeError("u_accept and u_sample must be float32")
-    b, T, V = target_logits.shape
-    depth_n = draft_logits.shape[1]
-    if draft_logits.shape != (b, depth_n, V) or tuple(u_accept.shape) != (b, T) or \
-            tuple(u_sample.shape) != (b,):
+    if tuple(u_accept.shape) != (b, T) or tuple(u_sample.shape) != (b,):
         raise ValueError("inconsistent shapes")
     dev = target_logits.device
     alen = torch.empty((b,), dtype=torch.int32, device=dev)
@@ -281,9 +305,10 @@ def jt_accept_stochastic(target_logits, draft_logits, parent, token, depth, n_no
     bonus = torch.empty((b,), dtype=torch.int32, device=dev)
     ws = workspace if workspace is not None else _workspace(
         lib.jt_accept_stochastic_workspace(b, V), dev)
+    dr = draft_logits if draft_mode == "sampled" else None
     _check("jt_accept_stochastic", lib.jt_accept_stochastic(
-        _ptr(target_logits), _ptr(draft_logits), _dtype_code(target_logits), b, T, V, depth_n,
-        _ptr(parent), _ptr(token), _ptr(depth), _ptr(n_nodes), float(temperature), _ptr(u_accept),
-        _ptr(u_sample), _ptr(alen), _ptr(anodes), _ptr(bonus), _ptr(err), _ptr(ws), ws.numel(),
-        _stream()))
+        _ptr(target_logits), _ptr(dr), _dtype_code(target_logits), b, T, V, depth_n,
+        _ptr(parent), _ptr(token), _ptr(depth), _ptr(n_nodes), float(temperature),
+        modes[draft_mode], _ptr(u_accept), _ptr(u_sample), _ptr(alen), _ptr(anodes), _ptr(bonus),
+        _ptr(err), _ptr(ws), ws.numel(), _stream()))
     return alen, anodes, bonus

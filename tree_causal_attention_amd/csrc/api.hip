@@ -33,7 +33,7 @@ const char* jt_status_string(jt_status s) {
   return "unknown status";
 }
 
-int jt_version(void) { return 100; }
+int jt_version(void) { return 200; }
 
 size_t jt_build_tree_workspace(int batch, int depth_n, int vocab, int width_w, int budget_b) {
   (void)budget_b;
@@ -192,10 +192,14 @@ jt_status jt_accept(const void* target_logits, jt_dtype dt, int batch, int max_n
 
 jt_status jt_accept_margin(const void* target_logits, jt_dtype dt, int batch, int max_nodes,
                            int vocab, int depth_n, const int32_t* parent, const int32_t* token,
-                           const int32_t* depth, const int32_t* n_nodes, double logit_margin,
-                           int32_t* accept_len, int32_t* accept_nodes, int32_t* bonus_token,
-                           int32_t* err, void* workspace, size_t workspace_bytes,
-                           void* stream) {
+                           const int32_t* depth, const int32_t* n_nodes, double theta,
+                           double temperature, int32_t* accept_len, int32_t* accept_nodes,
+                           int32_t* bonus_token, int32_t* err, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  if (!(theta > 0.0 && theta <= 1.0)) return JT_ERR_INVALID_ARG;
+  if (!(temperature > 0.0) || !std::isfinite(temperature)) return JT_ERR_INVALID_ARG;
+  // p(x) / p(top1) >= theta with p = softmax(L / T)  <=>  L[x] - max L >= T ln(theta)
+  const double logit_margin = temperature * std::log(theta);
   return accept_common(target_logits, dt, batch, max_nodes, vocab, depth_n, parent, token,
                        depth, n_nodes, accept_len, accept_nodes, bonus_token, err, workspace,
                        workspace_bytes, stream, 1, logit_margin);
@@ -231,24 +235,27 @@ size_t jt_accept_stochastic_workspace(int batch, int vocab) {
 jt_status jt_accept_stochastic(const void* target_logits, const void* draft_logits, jt_dtype dt,
                                int batch, int max_nodes, int vocab, int depth_n,
                                const int32_t* parent, const int32_t* token, const int32_t* depth,
-                               const int32_t* n_nodes, float temperature, const float* u_accept,
+                               const int32_t* n_nodes, float temperature,
+                               jt_draft_mode draft_mode, const float* u_accept,
                                const float* u_sample, int32_t* accept_len, int32_t* accept_nodes,
                                int32_t* bonus_token, int32_t* err, void* workspace,
                                size_t workspace_bytes, void* stream) {
   if (batch < 0 || max_nodes < 1 || vocab < 1 || depth_n < 1 || !valid_dtype(dt))
     return JT_ERR_INVALID_ARG;
   if (!(temperature > 0.0f) || !std::isfinite(temperature)) return JT_ERR_INVALID_ARG;
+  if (draft_mode != JT_DRAFT_TOPW && draft_mode != JT_DRAFT_SAMPLED) return JT_ERR_INVALID_ARG;
   if (max_nodes > kMaxNodes || depth_n > kMaxDepth) return JT_ERR_UNSUPPORTED;
   if (batch == 0) return JT_OK;
-  if (!target_logits || !draft_logits || !parent || !token || !depth || !n_nodes || !u_accept ||
-      !u_sample || !accept_len || !accept_nodes || !bonus_token)
+  const bool sampled = draft_mode == JT_DRAFT_SAMPLED;
+  if (!target_logits || (sampled && !draft_logits) || !parent || !token || !depth || !n_nodes ||
+      !u_accept || !u_sample || !accept_len || !accept_nodes || !bonus_token)
     return JT_ERR_INVALID_ARG;
   const size_t need = jt::accept_stochastic_workspace_bytes(batch, vocab);
   if (!workspace || workspace_bytes < need) return JT_ERR_WORKSPACE;
   return launched(jt::accept_stochastic_launch(
       target_logits, draft_logits, dt, batch, max_nodes, vocab, depth_n, parent, token, depth,
-      n_nodes, temperature, u_accept, u_sample, accept_len, accept_nodes, bonus_token, err,
-      workspace, static_cast<hipStream_t>(stream)));
+      n_nodes, temperature, u_accept, u_sample, sampled ? 1 : 0, accept_len, accept_nodes,
+      bonus_token, err, workspace, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -57,22 +57,24 @@ hipError_t accept_launch(const void* logits, jt_dtype dt, int batch, int max_nod
                          int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
                          void* workspace, hipStream_t stream, int mode, double margin);
 
-// commit.hip
+// stochastic.hip
 hipError_t accept_stochastic_launch(const void* target, const void* draft, jt_dtype dt,
                                     int batch, int max_nodes, int vocab, int depth_n,
                                     const int32_t* parent, const int32_t* token,
                                     const int32_t* depth, const int32_t* n_nodes,
                                     float temperature, const float* u_accept,
-                                    const float* u_sample, int32_t* accept_len,
+                                    const float* u_sample, int sampled, int32_t* accept_len,
                                     int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
                                     void* workspace, hipStream_t stream);
 size_t accept_stochastic_workspace_bytes(int batch, int vocab);
+// build_tree.hip (variants)
 hipError_t build_tree_variant_launch(const void* logits, jt_dtype dt, int batch, int depth_n,
                                      int vocab, int width, int budget, int expand_mode,
                                      double entropy_weight, const int32_t* root_token,
                                      int32_t* parent, int32_t* token, int32_t* depth,
                                      double* score, int32_t* n_nodes, int32_t* err,
                                      void* workspace, hipStream_t stream);
+// commit.hip
 hipError_t commit_kv_launch(void* k_pool, void* v_pool, int elem_bytes, int batch, int hkv,
                             int head_dim, const int32_t* page_table, int max_pages,
                             int num_pages, const int32_t* n_nodes, int max_nodes, int depth_n,

@@ -6,26 +6,37 @@
 //
 // Tree walk (one workgroup of 1024 threads per sequence): at the current
 // node u, p = softmax(target row u / T); its children (node-index order = their
-// candidate rank) are tried in turn with q = softmax(draft row depth / T) of
-// their depth: child v (token x) is accepted iff u_accept[v] * q(x) < p(x);
-// a rejection replaces p by norm(max(0, p - q)).  With q fixed inside one
-// node's child list, k rejections leave p_k proportional to
-// max(0, p - s_k q), s_0 = 0, s_{k+1} = s_k + sum_y max(0, p - s_k q).
-// The kernel keeps that in unnormalised form: with et = exp((x - max) / T)
-// of the target row (sum zt), ed the same for the draft row (sum zd) and
-// c = s zt / zd, the residual weights are max(0, et - c ed), their sum U, and
-// a rejection sets c += U / zd.  The accept test reads
-//   u_accept * ed[x] / zd < max(0, et[x] - c ed[x]) / U,
-// the same inequality as u q(x) < p_k(x) up to rounding.  et and ed are kept
-// in the workspace, so every pass after the row statistics is one fused
-// multiply-add per entry.  When no child is accepted the bonus token is the
-// inverse-CDF draw of u_sample over the residual weights.  All probability
-// arithmetic is fp64 (exp from the device math library).
+// candidate rank) are tried in turn; an accepted child becomes the current
+// node; when none is accepted the bonus token is the inverse-CDF draw of
+// u_sample over the current residual.  What q is depends on the proposal:
 //
-// Every walk starts at the root with the depth-1 draft row, so the statistics
-// of those two rows are computed beforehand across the whole GPU (chunk
-// maxima, then the exponentials and per-chunk fp64 sums); the walk adds the
-// chunk sums in chunk order and computes deeper rows itself.
+// * Top-W siblings (JT_DRAFT_TOPW; the trees jt_build_tree makes: JetSpec news
+//   piece, tree-construction paragraph; explainer section 五).  The siblings
+//   are chosen, so each one's proposal is the point mass on its token: x is
+//   accepted iff u_accept < p_k(x), and a rejection removes x from p and
+//   renormalises.  With et = exp((x - max) / T) of the target row (sum zt)
+//   and R the rejected mass, p_k(x) = et[x] / (zt - R); a rejected token's
+//   et entry is set to zero, so the bonus draw and a repeated token see it
+//   removed.  No pass over the vocabulary follows a rejection.
+// * Children drawn i.i.d. from q = softmax(draft row depth / T)
+//   (JT_DRAFT_SAMPLED).  Child v (token x) is accepted iff
+//   u_accept[v] * q(x) < p(x); a rejection replaces p by norm(max(0, p - q)).
+//   With q fixed inside one node's child list, k rejections leave p_k
+//   proportional to max(0, p - s_k q), s_0 = 0,
+//   s_{k+1} = s_k + sum_y max(0, p - s_k q).  The kernel keeps that in
+//   unnormalised form: with ed the exponentials of the draft row (sum zd) and
+//   c = s zt / zd, the residual weights are max(0, et - c ed), their sum U,
+//   and a rejection sets c += U / zd.  The accept test reads
+//     u_accept * ed[x] / zd < max(0, et[x] - c ed[x]) / U,
+//   the same inequality as u q(x) < p_k(x) up to rounding.  Every pass after
+//   the row statistics is one fused multiply-add per entry.
+// All probability arithmetic is fp64 (exp from the device math library).
+//
+// Every walk starts at the root (and, with sampled children, the depth-1
+// draft row), so the statistics of those rows are computed beforehand across
+// the whole GPU (chunk maxima, then the exponentials, per-chunk fp64 sums and
+// counts of positive weights); the walk adds the chunk sums in chunk order and
+// computes deeper rows itself.
 #include "jt_device.h"
 #include "jt_host.h"
 
@@ -42,9 +53,10 @@ constexpr int kPreChunk = kPreThreads * 16;  // entries of one pre-pass workgrou
 
 // Workspace: et and ed (2 * vocab doubles per sequence), then per sequence
 // and pre-pass row (0: the root's target row, 1: the depth-1 draft row) the
-// chunk sums (double), maxima (float) and bad flags (int).
+// chunk sums (double), maxima (float), bad flags (int) and counts of positive
+// exponentials (int).
 struct StWorkspace {
-  size_t off_sum, off_max, off_bad, bytes;
+  size_t off_sum, off_max, off_bad, off_pos, bytes;
   int nch;
 };
 
@@ -55,7 +67,8 @@ static __host__ __device__ StWorkspace st_workspace(int batch, int vocab) {
   w.off_sum = (static_cast<size_t>(batch) * 2 * vocab * sizeof(double) + 255) / 256 * 256;
   w.off_max = w.off_sum + cells * sizeof(double);
   w.off_bad = w.off_max + cells * sizeof(float);
-  w.bytes = w.off_bad + cells * sizeof(int);
+  w.off_pos = w.off_bad + cells * sizeof(int);
+  w.bytes = w.off_pos + cells * sizeof(int);
   return w;
 }
 
@@ -70,11 +83,13 @@ __device__ __forceinline__ const T* pre_row(const T* target, const T* draft, int
 template <typename T>
 __global__ __launch_bounds__(kPreThreads) void stoch_pre_max(
     const T* __restrict__ target, const T* __restrict__ draft, int max_nodes, int vocab,
-    int depth_n, int nch, float* __restrict__ cmax, int* __restrict__ cbad) {
+    int depth_n, int nch, int nrows, float* __restrict__ cmax, int* __restrict__ cbad) {
   __shared__ float rm[kPreThreads / kWave];
   __shared__ int rb[kPreThreads / kWave];
-  // workgroup = (chunk, row, sequence), chunk fastest
-  const int c = blockIdx.x % nch, r = (blockIdx.x / nch) % 2, seq = blockIdx.x / nch / 2;
+  // workgroup = (chunk, row, sequence), chunk fastest; nrows = 1 (root target
+  // row only) or 2 (and the depth-1 draft row)
+  const int c = blockIdx.x % nch, r = (blockIdx.x / nch) % nrows,
+            seq = blockIdx.x / nch / nrows;
   const T* row = pre_row(target, draft, seq, r, max_nodes, depth_n, vocab);
   float m = -INFINITY;
   int b = 0;
@@ -105,19 +120,24 @@ __global__ __launch_bounds__(kPreThreads) void stoch_pre_max(
 }
 
 // Pre-pass 2: row maximum from the chunk maxima, then exp((x - max) / T) into
-// et (r = 0) or ed (r = 1) and the chunk's fp64 sum (fixed summation order).
+// et (r = 0) or ed (r = 1), the chunk's fp64 sum (fixed summation order) and
+// its count of positive exponentials.
 template <typename T>
 __global__ __launch_bounds__(kPreThreads) void stoch_pre_exp(
     const T* __restrict__ target, const T* __restrict__ draft, int max_nodes, int vocab,
-    int depth_n, int nch, double tinv, const float* __restrict__ cmax,
-    const int* __restrict__ cbad, double* __restrict__ csum, double* __restrict__ ecache) {
+    int depth_n, int nch, int nrows, double tinv, const float* __restrict__ cmax,
+    const int* __restrict__ cbad, double* __restrict__ csum, int* __restrict__ cpos,
+    double* __restrict__ ecache) {
   __shared__ double rs[kPreThreads / kWave];
-  const int c = blockIdx.x % nch, r = (blockIdx.x / nch) % 2, seq = blockIdx.x / nch / 2;
+  __shared__ int rp[kPreThreads / kWave];
+  const int c = blockIdx.x % nch, r = (blockIdx.x / nch) % nrows,
+            seq = blockIdx.x / nch / nrows;
   const size_t cell0 = (static_cast<size_t>(seq) * 2 + r) * nch;
   float m = -INFINITY;
   int b = 0;
   for (int k = 0; k < nch; ++k) { m = fmaxf(m, cmax[cell0 + k]); b |= cbad[cell0 + k]; }
   double z = 0.0;
+  int pos = 0;
   if (!b && m != -INFINITY) {
     const T* row = pre_row(target, draft, seq, r, max_nodes, depth_n, vocab);
     double* e_out = ecache + (static_cast<size_t>(seq) * 2 + r) * vocab;
@@ -134,16 +154,21 @@ __global__ __launch_bounds__(kPreThreads) void stoch_pre_exp(
         const double e = exp((static_cast<double>(x[k]) - static_cast<double>(m)) * tinv);
         e_out[i] = e;
         z += e;
+        pos += e > 0.0;
       }
     }
   }
-  for (int o = 32; o > 0; o >>= 1) z += __shfl_xor(z, o, kWave);
+  for (int o = 32; o > 0; o >>= 1) {
+    z += __shfl_xor(z, o, kWave);
+    pos += __shfl_xor(pos, o, kWave);
+  }
   const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-  if (lane == 0) rs[wv] = z;
+  if (lane == 0) { rs[wv] = z; rp[wv] = pos; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int k = 1; k < kPreThreads / kWave; ++k) z += rs[k];
+    for (int k = 1; k < kPreThreads / kWave; ++k) { z += rs[k]; pos += rp[k]; }
     csum[cell0 + c] = z;
+    cpos[cell0 + c] = pos;
   }
 }
 
@@ -205,13 +230,25 @@ __device__ __forceinline__ int block_or(int v, int* red) {
   return t;
 }
 
+__device__ __forceinline__ int block_add(int v, int* red) {
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
+  __syncthreads();
+  if (lane == 0) red[wv] = v;
+  __syncthreads();
+  int t = 0;
+  for (int k = 0; k < kStWaves; ++k) t += red[k];
+  return t;
+}
+
 // Row statistics: max (exact) and Z = sum exp((x - max) / T) in fp64; every
-// exp((x - max) / T) is also stored in e_out[i] for the later passes.  Sets
-// *bad for NaN / +inf entries or a row without a finite entry.
+// exp((x - max) / T) is also stored in e_out[i] for the later passes, and
+// *pos_out counts the positive ones.  Sets *bad for NaN / +inf entries or a
+// row without a finite entry.
 template <typename T>
 __device__ void row_stats(RowView<T> r, int vocab, double tinv, float* m_out, double* z_out,
-                          bool* bad, double* __restrict__ e_out, float* redf, double* redd,
-                          int* redi) {
+                          int* pos_out, bool* bad, double* __restrict__ e_out, float* redf,
+                          double* redd, int* redi) {
   float m = -INFINITY;
   int b = 0;
   // 4-entry loads when the row allows them (one load request per 4 entries:
@@ -254,6 +291,7 @@ __device__ void row_stats(RowView<T> r, int vocab, double tinv, float* m_out, do
   m = block_max(m, redf);
   b = block_or(b, redi);
   double z = 0.0;
+  int pos = 0;
   if (!b && m != -INFINITY && vec) {
     const int v4 = vocab / 4;
     double2* e2 = reinterpret_cast<double2*>(e_out);
@@ -274,6 +312,7 @@ __device__ void row_stats(RowView<T> r, int vocab, double tinv, float* m_out, do
           for (int q = 0; q < 4; ++q) {
             e[q] = exp((static_cast<double>(x[k][q]) - static_cast<double>(m)) * tinv);
             z += e[q];
+            pos += e[q] > 0.0;
           }
           e2[2 * j] = make_double2(e[0], e[1]);
           e2[2 * j + 1] = make_double2(e[2], e[3]);
@@ -295,10 +334,12 @@ __device__ void row_stats(RowView<T> r, int vocab, double tinv, float* m_out, do
           const double e = exp((static_cast<double>(x[k]) - static_cast<double>(m)) * tinv);
           e_out[i] = e;
           z += e;
+          pos += e > 0.0;
         }
       }
     }
   z = block_sum(z, redd);  // its barriers also publish e_out to the workgroup
+  *pos_out = block_add(pos, redi);
   *m_out = m;
   *z_out = z;
   *bad = b || m == -INFINITY;
@@ -313,7 +354,7 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
     int32_t* __restrict__ accept_len, int32_t* __restrict__ accept_nodes,
     int32_t* __restrict__ bonus_token, int32_t* err, double* __restrict__ ecache,
     const double* __restrict__ pre_sum, const float* __restrict__ pre_max,
-    const int* __restrict__ pre_bad, int nch) {
+    const int* __restrict__ pre_bad, const int* __restrict__ pre_pos, int nch, int sampled) {
   __shared__ int par[1024];
   __shared__ float redf[kStWaves];
   __shared__ double redd[kStWaves];
@@ -369,33 +410,73 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
   const double tinv = 1.0 / static_cast<double>(temperature);
   // statistics of pre-pass row r (0: root target row, 1: depth-1 draft row),
   // whose exponentials are already in et / ed; chunk sums added in order
-  auto pre_stats = [&](int r, float* m_out, double* z_out, bool* bad) {
+  auto pre_stats = [&](int r, float* m_out, double* z_out, int* pos_out, bool* bad) {
     const size_t cell0 = (static_cast<size_t>(seq) * 2 + r) * nch;
     float m = -INFINITY;
-    int bb = 0;
+    int bb = 0, pos = 0;
     double z = 0.0;
     for (int k = 0; k < nch; ++k) {
       m = fmaxf(m, pre_max[cell0 + k]);
       bb |= pre_bad[cell0 + k];
       z += pre_sum[cell0 + k];
+      pos += pre_pos[cell0 + k];
     }
     *m_out = m;
     *z_out = z;
+    *pos_out = pos;
     *bad = bb || m == -INFINITY;
   };
-  const T* draft_seq = draft + static_cast<size_t>(seq) * depth_n * vocab;
   int u = 0, L = 0;
   // current distribution: weights max(0, et - c ed) over the current node's
   // target row (ed: the children's draft row), total U; c = 0 is plain p
   float mt = 0.0f, md = 0.0f;
   double zt = 1.0, zd = 1.0, c = 0.0, U = 1.0;
-  while (true) {
-    bool bad = false;
+  int npos = 0, npos_d = 0;
+  auto node_stats = [&](bool* bad) {
     if (u == 0)
-      pre_stats(0, &mt, &zt, &bad);
+      pre_stats(0, &mt, &zt, &npos, bad);
     else
-      row_stats(RowView<T>{target + (base + u) * vocab}, vocab, tinv, &mt, &zt, &bad, et, redf,
-                redd, redi);
+      row_stats(RowView<T>{target + (base + u) * vocab}, vocab, tinv, &mt, &zt, &npos, bad, et,
+                redf, redd, redi);
+  };
+  while (!sampled) {
+    // top-W siblings: point-mass proposals.  zt - R is the mass left after
+    // the rejected tokens (whose et entries are then zero).
+    bool bad = false;
+    node_stats(&bad);
+    if (bad) { fail(JT_DERR_BAD_LOGIT); return; }
+    double R = 0.0;
+    int npos_rej = 0;
+    int next = -1;
+    for (int v = u + 1; v < n; ++v) {
+      if (par[v] != u) continue;  // uniform: par is in LDS, v is uniform
+      const int x = token[base + v];
+      const double ex = et[x];
+      // the mass left still holds x itself (guards the rounding of zt - R)
+      if (static_cast<double>(u_accept[base + v]) < ex / fmax(zt - R, ex)) {
+        next = v;
+        break;
+      }
+      if (ex > 0.0) {
+        // removing the last positive weight would leave no mass: keep p
+        if (npos_rej + 1 == npos) break;
+        ++npos_rej;
+        R += ex;
+        __syncthreads();  // every thread has read et[x]
+        if (tid == 0) et[x] = 0.0;
+        __syncthreads();  // the removal is visible to later reads
+      }
+    }
+    if (next < 0) break;
+    if (tid == 0) path[L] = next;
+    ++L;
+    u = next;
+    __syncthreads();  // every thread is done with et before the next row overwrites it
+  }
+  const T* draft_seq = sampled ? draft + static_cast<size_t>(seq) * depth_n * vocab : nullptr;
+  while (sampled) {
+    bool bad = false;
+    node_stats(&bad);
     if (bad) { fail(JT_DERR_BAD_LOGIT); return; }
     c = 0.0;
     U = zt;
@@ -406,10 +487,10 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
       if (!have_q) {
         const int d = depth[base + v];
         if (d == 1)
-          pre_stats(1, &md, &zd, &bad);
+          pre_stats(1, &md, &zd, &npos_d, &bad);
         else
           row_stats(RowView<T>{draft_seq + static_cast<size_t>(d - 1) * vocab}, vocab, tinv, &md,
-                    &zd, &bad, ed, redf, redd, redi);
+                    &zd, &npos_d, &bad, ed, redf, redd, redi);
         if (bad) { fail(JT_DERR_BAD_LOGIT); return; }
         have_q = true;
       }
@@ -466,7 +547,8 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
     u = next;
     __syncthreads();  // every thread is done with et before the next row overwrites it
   }
-  // ---- bonus: inverse-CDF draw over the residual weights of the current node.
+  // ---- bonus: inverse-CDF draw over the residual weights of the current node
+  // (c == 0: the weights are et itself, with top-W rejections already zeroed).
   // Wave w owns a contiguous segment of the vocabulary, cut into kBonusBlocks
   // blocks (lanes read them coalesced).  One exclusive prefix over the block
   // sums in (wave, block) order finds the block whose interval holds
@@ -492,7 +574,7 @@ __global__ __launch_bounds__(kStThreads) void accept_stochastic_kernel(
         for (int k = 0; k < kStUnroll / 2; ++k) {
           const int i = i0 + k * kWave;
           a[k] = i < b1 / 2 ? et2[i] : make_double2(0.0, 0.0);
-          q[k] = i < b1 / 2 ? ed2[i] : make_double2(0.0, 0.0);
+          q[k] = (c != 0.0 && i < b1 / 2) ? ed2[i] : make_double2(0.0, 0.0);
         }
 #pragma unroll
         for (int k = 0; k < kStUnroll / 2; ++k) {
@@ -587,7 +669,7 @@ hipError_t accept_stochastic_launch(const void* target, const void* draft, jt_dt
                                     const int32_t* parent, const int32_t* token,
                                     const int32_t* depth, const int32_t* n_nodes,
                                     float temperature, const float* u_accept,
-                                    const float* u_sample, int32_t* accept_len,
+                                    const float* u_sample, int sampled, int32_t* accept_len,
                                     int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
                                     void* workspace, hipStream_t stream) {
   unsigned char* ws = static_cast<unsigned char*>(workspace);
@@ -596,20 +678,26 @@ hipError_t accept_stochastic_launch(const void* target, const void* draft, jt_dt
   double* csum = reinterpret_cast<double*>(ws + L.off_sum);
   float* cmax = reinterpret_cast<float*>(ws + L.off_max);
   int* cbad = reinterpret_cast<int*>(ws + L.off_bad);
+  int* cpos = reinterpret_cast<int*>(ws + L.off_pos);
   const double tinv = 1.0 / static_cast<double>(temperature);
-  const dim3 pre_grid(static_cast<unsigned>(L.nch) * 2u * static_cast<unsigned>(batch));
+  // rows computed up front: the root's target row, plus the depth-1 draft row
+  // when children are sampled from the draft
+  const int nrows = sampled ? 2 : 1;
+  const dim3 pre_grid(static_cast<unsigned>(L.nch) * static_cast<unsigned>(nrows) *
+                      static_cast<unsigned>(batch));
 #define JT_ST_LAUNCH(TT)                                                                        \
   do {                                                                                          \
     const TT* tg = static_cast<const TT*>(target);                                              \
     const TT* dr = static_cast<const TT*>(draft);                                               \
     hipLaunchKernelGGL(stoch_pre_max<TT>, pre_grid, dim3(kPreThreads), 0, stream, tg, dr,       \
-                       max_nodes, vocab, depth_n, L.nch, cmax, cbad);                           \
+                       max_nodes, vocab, depth_n, L.nch, nrows, cmax, cbad);                    \
     hipLaunchKernelGGL(stoch_pre_exp<TT>, pre_grid, dim3(kPreThreads), 0, stream, tg, dr,       \
-                       max_nodes, vocab, depth_n, L.nch, tinv, cmax, cbad, csum, ecache);       \
+                       max_nodes, vocab, depth_n, L.nch, nrows, tinv, cmax, cbad, csum, cpos,   \
+                       ecache);                                                                 \
     hipLaunchKernelGGL(accept_stochastic_kernel<TT>, dim3(batch), dim3(kStThreads), 0, stream,  \
                        tg, dr, max_nodes, vocab, depth_n, parent, token, depth, n_nodes,        \
                        temperature, u_accept, u_sample, accept_len, accept_nodes, bonus_token,  \
-                       err, ecache, csum, cmax, cbad, L.nch);                                   \
+                       err, ecache, csum, cmax, cbad, cpos, L.nch, sampled);                    \
   } while (0)
   if (dt == JT_F32)
     JT_ST_LAUNCH(float);
