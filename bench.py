@@ -347,7 +347,7 @@ def time_next_rows(B, w, x, tree, d_draft, d_target, d_k, d_v, d_prefix, d_table
     pref = d_prefix.clone()
     out["commit_kv_us"] = timed(
         lambda: B.jt_commit_kv(d_k, d_v, d_table, x.num_pages, nn, T, d_alen, d_anodes, pref,
-                               err=err),
+                               parent=par, err=err),
         before=lambda: pref.copy_(d_prefix))
     out["commit_kv_rows"] = int(alen.sum())
     # build-mode variants (sequential best-first) next to the default build

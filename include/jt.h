@@ -324,21 +324,29 @@ jt_status jt_accept_margin(const void* target_logits, jt_dtype dt, int batch, in
  *   page_table      [batch, max_pages_per_seq] int32 (as jt_tree_attention).
  *                   Tail pages must not be shared between sequences.
  *   n_nodes         [batch] int32 (the tree's node count).
+ *   parent          [batch, max_nodes] int32 (nullable): the tree's parent
+ *                   array; when given, accept_nodes must also be the chain
+ *                   root -> a_1 -> ... -> a_L (parent[a_1] = 0,
+ *                   parent[a_k] = a_{k-1}).
  *   accept_len      [batch] int32; accept_nodes [batch, depth_n] int32 (as
  *                   from jt_accept / jt_accept_margin).
  *   prefix_len      [batch] int32 (in/out).
  *   err             JT_DERR_BAD_PATH (accept_len outside [0, min(depth_n,
  *                   n_nodes - 1)], accept_nodes not strictly increasing in
- *                   [1, n_nodes), n_nodes or prefix_len invalid), JT_DERR_BAD_PAGE;
- *                   such a sequence is left unchanged.
+ *                   [1, n_nodes) or, with parent, not a root-to-node chain,
+ *                   n_nodes or prefix_len invalid), JT_DERR_BAD_PAGE (a page
+ *                   id of a moved row's source or destination outside
+ *                   [0, num_pages)).  Such a sequence is left unchanged: its
+ *                   pools and its prefix_len are not written.
  * Limits: page_size == 16, head_dim * element size a multiple of 16 bytes,
  * 1 <= depth_n <= 64 with 2 * depth_n * head_dim * element size <= 64 KiB,
  * 1 <= max_nodes <= 1024.
  * ---------------------------------------------------------------------- */
 jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int num_kv_heads,
                        int head_dim, const int32_t* page_table, int max_pages_per_seq,
-                       int num_pages, int page_size, const int32_t* n_nodes, int max_nodes,
-                       int depth_n, const int32_t* accept_len, const int32_t* accept_nodes,
+                       int num_pages, int page_size, const int32_t* n_nodes,
+                       const int32_t* parent, int max_nodes, int depth_n,
+                       const int32_t* accept_len, const int32_t* accept_nodes,
                        int32_t* prefix_len, int32_t* err, void* stream);
 
 /* ------------------------------------------------------------------------

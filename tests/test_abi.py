@@ -150,7 +150,7 @@ def test_commit_kv_validation(lib):
     p = ctypes.c_void_p(1)
 
     def call(dt=1, b=1, hkv=2, D=128, maxp=4, npages=8, ps=16, T=17, N=16):
-        return f(p, p, dt, b, hkv, D, p, maxp, npages, ps, p, T, N, p, p, p, None, None)
+        return f(p, p, dt, b, hkv, D, p, maxp, npages, ps, p, None, T, N, p, p, p, None, None)
 
     assert call(ps=32) == B.JT_ERR_UNSUPPORTED
     assert call(D=4) == B.JT_ERR_UNSUPPORTED        # 8-byte rows

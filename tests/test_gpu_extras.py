@@ -180,8 +180,11 @@ def _commit_case(rng, b, hkv, D, dtype, T=40, N=16):
     anodes = np.full((b, N), -1, dtype=np.int32)
     for s in range(b):
         anodes[s, :alen[s]] = paths[s]
+    par = np.full((b, T), -1, dtype=np.int32)
+    for s in range(b):
+        par[s, :ns[s]] = pars[s]
     return dict(k=k, v=v, table=table, total=total, P=np.array(prefixes, dtype=np.int32),
-                n=np.array(ns, dtype=np.int32), alen=alen, anodes=anodes, T=T, N=N)
+                n=np.array(ns, dtype=np.int32), alen=alen, anodes=anodes, T=T, N=N, par=par)
 
 
 def _bits(t):
@@ -198,14 +201,15 @@ def _oracle_commit(c, seqs):
     return kr, vr, Ps
 
 
-def _gpu_commit(c, err_expected=0):
+def _gpu_commit(c, with_parent=False):
     d = dev()
     k, v = c["k"].to(d), c["v"].to(d)
     P = torch.from_numpy(c["P"].copy()).to(d)
     err = torch.zeros(1, dtype=torch.int32, device=d)
+    par = torch.from_numpy(c["par"]).to(d) if with_parent else None
     B.jt_commit_kv(k, v, torch.from_numpy(c["table"]).to(d), c["total"],
                    torch.from_numpy(c["n"]).to(d), c["T"], torch.from_numpy(c["alen"]).to(d),
-                   torch.from_numpy(c["anodes"]).to(d), P, err=err)
+                   torch.from_numpy(c["anodes"]).to(d), P, parent=par, err=err)
     torch.cuda.synchronize()
     return k.cpu(), v.cpu(), P.cpu().numpy(), int(err.item())
 
@@ -220,6 +224,71 @@ def test_commit_bit_exact(seed, hkv, D, dtype):
     kg, vg, Pg, err = _gpu_commit(c)
     assert err == 0
     kr, vr, Ps = _oracle_commit(c, range(len(c["P"])))
+    for s, P2 in Ps.items():
+        assert int(Pg[s]) == P2
+    assert np.array_equal(_bits(kg), kr) and np.array_equal(_bits(vg), vr)
+
+
+@pytest.mark.parametrize("with_parent", [False, True])
+def test_commit_bit_exact_parent_checked(with_parent):
+    rng = np.random.default_rng(808)
+    c = _commit_case(rng, 8, 2, 128, "bf16")
+    kg, vg, Pg, err = _gpu_commit(c, with_parent=with_parent)
+    assert err == 0
+    kr, vr, Ps = _oracle_commit(c, range(len(c["P"])))
+    assert [int(Pg[s]) for s in Ps] == [Ps[s] for s in Ps]
+    assert np.array_equal(_bits(kg), kr) and np.array_equal(_bits(vg), vr)
+
+
+def _force_path(c, s, rng):
+    """Sequence s gets a tree with a chain of at least 3 accepted nodes."""
+    n = max(int(c["n"][s]), 6)
+    c["n"][s] = n
+    c["par"][s, :] = -1
+    c["par"][s, :n] = [-1, 0, 1, 2] + [0] * (n - 4)
+    c["alen"][s] = 3
+    c["anodes"][s, :] = -1
+    c["anodes"][s, :3] = [1, 2, 3]
+
+
+def test_commit_non_chain_rejected_with_parent():
+    """accept_nodes strictly increasing but not a root-to-node chain (node 4
+    hangs off the root): rejected when the parent array is given, the
+    sequence's pools and prefix untouched; without it only the increasing
+    order is checked and the rows are moved."""
+    rng = np.random.default_rng(31)
+    c = _commit_case(rng, 3, 2, 64, "bf16")
+    _force_path(c, 1, rng)
+    c["anodes"][1, :3] = [1, 2, 4]
+    kg, vg, Pg, err = _gpu_commit(c, with_parent=True)
+    assert err == B.DERR_BAD_PATH
+    assert int(Pg[1]) == int(c["P"][1])
+    kr, vr, Ps = _oracle_commit(c, (0, 2))
+    for s, P2 in Ps.items():
+        assert int(Pg[s]) == P2
+    assert np.array_equal(_bits(kg), kr) and np.array_equal(_bits(vg), vr)
+    kg, vg, Pg, err = _gpu_commit(c, with_parent=False)
+    assert err == 0
+    kr, vr, Ps = _oracle_commit(c, (0, 1, 2))
+    assert int(Pg[1]) == Ps[1]
+    assert np.array_equal(_bits(kg), kr) and np.array_equal(_bits(vg), vr)
+
+
+@pytest.mark.parametrize("where", ["source", "destination"])
+def test_commit_bad_page_leaves_sequence_unchanged(where):
+    """A page id outside the pool under one of the moved rows (a source row
+    P + a_k, or a destination row P + k): reported, the sequence keeps its
+    pools and its prefix length, the other sequences are committed."""
+    rng = np.random.default_rng(77 if where == "source" else 78)
+    c = _commit_case(rng, 3, 2, 64, "bf16")
+    _force_path(c, 1, rng)
+    P = int(c["P"][1])
+    t = P + int(c["anodes"][1, 2]) if where == "source" else P + 1
+    c["table"][1, t // 16] = c["total"] + 3 if where == "source" else -5
+    kg, vg, Pg, err = _gpu_commit(c, with_parent=True)
+    assert err == B.DERR_BAD_PAGE
+    assert int(Pg[1]) == P
+    kr, vr, Ps = _oracle_commit(c, (0, 2))
     for s, P2 in Ps.items():
         assert int(Pg[s]) == P2
     assert np.array_equal(_bits(kg), kr) and np.array_equal(_bits(vg), vr)

@@ -48,7 +48,7 @@ SIGNATURES = {
                                   ctypes.c_double, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
                                   _c_size, _vp]),
     "jt_commit_kv": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _vp, _c_int, _c_int, _c_int,
-                              _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
+                              _vp, _vp, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp]),
     "jt_accept_stochastic_workspace": (_c_size, [_c_int, _c_int]),
     "jt_accept_stochastic": (_c_int, [_vp, _vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp,
                                       _vp, _vp, _c_float, _c_int, _vp, _vp, _vp, _vp, _vp, _vp, _vp,
@@ -253,8 +253,12 @@ def jt_accept_margin(target_logits, depth_n: int, parent, token, depth, n_nodes,
 
 
 def jt_commit_kv(k_pool, v_pool, page_table, num_pages, n_nodes, max_nodes: int, accept_len,
-                 accept_nodes, prefix_len, err=None):
-    """Moves the accepted rows next to the prefix in place; advances prefix_len in place."""
+                 accept_nodes, prefix_len, parent=None, err=None):
+    """Moves the accepted rows next to the prefix in place; advances prefix_len in place.
+
+    parent [b, max_nodes] int32 (optional): when given, accept_nodes must
+    also form a root-to-node chain of that tree.
+    """
     lib = load()
     for t, nm in ((k_pool, "k_pool"), (v_pool, "v_pool"), (page_table, "page_table"),
                   (accept_nodes, "accept_nodes"), (prefix_len, "prefix_len")):
@@ -264,7 +268,7 @@ def jt_commit_kv(k_pool, v_pool, page_table, num_pages, n_nodes, max_nodes: int,
     depth_n = accept_nodes.shape[1]
     _check("jt_commit_kv", lib.jt_commit_kv(
         _ptr(k_pool), _ptr(v_pool), _dtype_code(k_pool), b, hkv, D, _ptr(page_table), maxp,
-        int(num_pages), ps, _ptr(n_nodes), int(max_nodes), depth_n, _ptr(accept_len),
+        int(num_pages), ps, _ptr(n_nodes), _ptr(parent), int(max_nodes), depth_n, _ptr(accept_len),
         _ptr(accept_nodes), _ptr(prefix_len), _ptr(err), _stream()))
 
 

@@ -207,8 +207,9 @@ jt_status jt_accept_margin(const void* target_logits, jt_dtype dt, int batch, in
 
 jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int num_kv_heads,
                        int head_dim, const int32_t* page_table, int max_pages_per_seq,
-                       int num_pages, int page_size, const int32_t* n_nodes, int max_nodes,
-                       int depth_n, const int32_t* accept_len, const int32_t* accept_nodes,
+                       int num_pages, int page_size, const int32_t* n_nodes,
+                       const int32_t* parent, int max_nodes, int depth_n,
+                       const int32_t* accept_len, const int32_t* accept_nodes,
                        int32_t* prefix_len, int32_t* err, void* stream) {
   if (batch < 0 || num_kv_heads < 1 || head_dim < 1 || max_pages_per_seq < 1 || num_pages < 1 ||
       max_nodes < 1 || depth_n < 1 || !valid_dtype(dt))
@@ -223,8 +224,9 @@ jt_status jt_commit_kv(void* k_pool, void* v_pool, jt_dtype dt, int batch, int n
     return JT_ERR_INVALID_ARG;
   return launched(jt::commit_kv_launch(k_pool, v_pool, dt == JT_F32 ? 4 : 2, batch, num_kv_heads,
                                        head_dim, page_table, max_pages_per_seq, num_pages,
-                                       n_nodes, max_nodes, depth_n, accept_len, accept_nodes,
-                                       prefix_len, err, static_cast<hipStream_t>(stream)));
+                                       n_nodes, parent, max_nodes, depth_n, accept_len,
+                                       accept_nodes, prefix_len, err,
+                                       static_cast<hipStream_t>(stream)));
 }
 
 size_t jt_accept_stochastic_workspace(int batch, int vocab) {

@@ -77,8 +77,9 @@ hipError_t build_tree_variant_launch(const void* logits, jt_dtype dt, int batch,
 // commit.hip
 hipError_t commit_kv_launch(void* k_pool, void* v_pool, int elem_bytes, int batch, int hkv,
                             int head_dim, const int32_t* page_table, int max_pages,
-                            int num_pages, const int32_t* n_nodes, int max_nodes, int depth_n,
-                            const int32_t* accept_len, const int32_t* accept_nodes,
-                            int32_t* prefix_len, int32_t* err, hipStream_t stream);
+                            int num_pages, const int32_t* n_nodes, const int32_t* parent,
+                            int max_nodes, int depth_n, const int32_t* accept_len,
+                            const int32_t* accept_nodes, int32_t* prefix_len, int32_t* err,
+                            hipStream_t stream);
 
 }  // namespace jt
