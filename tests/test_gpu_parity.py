@@ -283,25 +283,26 @@ def _workload_attention(name, instance, oracle_trees, full_seqs, sample):
             check_lse(lg[s, i, heads], rl[i, heads], w.dtype, f"{name} seq {s} node {i}")
 
 
-@pytest.mark.parametrize("name,instance,full", [("tiny_f32", 0, [0]), ("qwen3_8b_b16", 0, [0]),
-                                                ("qwen3_8b_b256", 0, [0]),
-                                                ("qwen3_8b_b256", 3, [0])])
+@pytest.mark.parametrize("name,instance,full",
+                         [("tiny_f32", 0, [0]), ("qwen3_8b_b16", 0, [0])]
+                         + [("qwen3_8b_b256", i, [0]) for i in range(8)])
 def test_attention_workloads_full(name, instance, full, oracle_trees):
     _workload_attention(name, instance, oracle_trees, full, [])
 
 
-def test_attention_serving_sampled(oracle_trees):
-    samp = [(s, [0, 1, 100, 200, 256], [0, 7, 31]) for s in (0, 5, 15)]
-    _workload_attention("serving_b16", 0, oracle_trees, [], samp)
+@pytest.mark.parametrize("name,seqs", [("serving_b16", range(0, 16)),
+                                       ("serving_b32", range(0, 16)),
+                                       ("serving_b32", range(16, 32)),
+                                       ("qwen3_30b_a3b_b8", range(0, 8))])
+def test_attention_batched_workloads_every_row(name, seqs, oracle_trees):
+    """Every node and head of every sequence of the batched workloads (the
+    launch the benchmark times), against the oracle's dense per-head pass."""
+    _workload_attention(name, 0, oracle_trees, list(seqs), [])
 
 
-def test_attention_serving_b32_sampled(oracle_trees):
-    """The batch-32 serving shape: sequences past the batch-16 ones."""
-    samp = [(s, [0, 2, 129, 256], [1, 16, 30]) for s in (16, 23, 31)]
-    _workload_attention("serving_b32", 0, oracle_trees, [], samp)
-
-
-def test_attention_long_prefix_sampled(oracle_trees):
+def test_attention_long_prefix_sampled_rows_reference_form(oracle_trees):
+    """A few rows of the 32K-prefix batch against the oracle's plain
+    per-(node, head) form, a second formulation of the same definition."""
     samp = [(s, [0, 3, 128, 255, 256], [0, 9, 31]) for s in (0, 7)]
     _workload_attention("qwen3_30b_a3b_b8", 0, oracle_trees, [], samp)
 
@@ -374,10 +375,13 @@ def test_accept_small_random_trees(seed):
         assert np.array_equal(anodes[s], nodes)
 
 
-@pytest.mark.parametrize("name,instance,plant", [("tiny_f32", 0, True), ("qwen3_8b_b16", 0, False),
-                                                 ("qwen3_8b_b256", 0, True),
-                                                 ("qwen3_8b_b256", 3, True),
-                                                 ("serving_b32", 0, True)])
+@pytest.mark.parametrize("name,instance,plant",
+                         [("tiny_f32", 0, True), ("qwen3_8b_b16", 0, False),
+                          ("qwen3_8b_b16", 0, True)]
+                         + [("qwen3_8b_b256", i, True) for i in range(8)]
+                         + [("qwen3_8b_b256", 1, False), ("serving_b16", 0, True),
+                            ("serving_b32", 0, True), ("qwen3_30b_a3b_b8", 0, True),
+                            ("qwen3_30b_a3b_b8", 0, False)])
 def test_accept_workloads(name, instance, plant, oracle_trees):
     w = WL.WORKLOADS[name]
     _say(f"accept {name}#{instance}")
