@@ -54,7 +54,8 @@ typedef enum {
   JT_ERR_INVALID_ARG = 1,  /* a null pointer, a negative or inconsistent size */
   JT_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement    */
   JT_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than the query says    */
-  JT_ERR_LAUNCH = 4        /* a HIP kernel launch failed                       */
+  JT_ERR_LAUNCH = 4,       /* a HIP kernel launch failed                       */
+  JT_ERR_SCRATCH = 5       /* inputs exceed jt_accept_noalloc's static scratch */
 } jt_status;
 
 typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
@@ -274,6 +275,31 @@ jt_status jt_accept(const void* target_logits, jt_dtype dt, int batch, int max_n
                     const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
                     int32_t* accept_nodes, int32_t* bonus_token, int32_t* err, void* workspace,
                     size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------
+ * jt_accept_noalloc -- jt_accept for callers that cannot allocate device
+ * memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc).
+ *
+ * Same arguments, outputs, rule and error bits as jt_accept, without the
+ * workspace: the argmax partials (8 bytes per (row, vocabulary chunk)) live
+ * in a static device array of JT_ACCEPT_SCRATCH_BYTES that each GPU the
+ * library runs on holds until the process ends.  The call allocates nothing
+ * (no hipMalloc / hipFree); its first call on a device looks up that
+ * device's copy of the array.  Inputs whose partials need more than the
+ * array (jt_accept_workspace(batch, max_nodes, vocab) > the limit, e.g.
+ * batch * max_nodes above about 64K rows) return JT_ERR_SCRATCH before
+ * anything is enqueued.  Every call on one GPU shares that GPU's array:
+ * calls that overlap on one GPU (concurrent streams or host threads) race
+ * and must be ordered by the caller.  Nothing in the array needs clearing
+ * between calls (every partial read is written first by the same call).
+ * ---------------------------------------------------------------------- */
+#define JT_ACCEPT_SCRATCH_BYTES (4u << 20)
+jt_status jt_accept_noalloc(const void* target_logits, jt_dtype dt, int batch, int max_nodes,
+                            int vocab, int depth_n, const int32_t* parent, const int32_t* token,
+                            const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
+                            int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
+                            void* stream);
 
 /* ------------------------------------------------------------------------
  * jt_accept_margin -- acceptance under the per-step margin rule.

@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_status_strings(lib):
-    for s in range(5):
+    for s in range(6):
         assert lib.jt_status_string(s)
     assert lib.jt_version() >= 100
 

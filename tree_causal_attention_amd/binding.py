@@ -20,7 +20,9 @@ LIB_PATH = os.path.join(HERE, "libjt.so")
 JT_F32, JT_BF16 = 0, 1
 JT_EXPAND_CANDIDATE, JT_EXPAND_NODE_BLOCK = 0, 1
 JT_DRAFT_TOPW, JT_DRAFT_SAMPLED = 0, 1
-JT_OK, JT_ERR_INVALID_ARG, JT_ERR_UNSUPPORTED, JT_ERR_WORKSPACE, JT_ERR_LAUNCH = range(5)
+JT_OK, JT_ERR_INVALID_ARG, JT_ERR_UNSUPPORTED, JT_ERR_WORKSPACE, JT_ERR_LAUNCH, JT_ERR_SCRATCH = (
+    range(6))
+ACCEPT_SCRATCH_BYTES = 4 << 20
 DERR_BAD_LOGIT, DERR_BAD_PARENT, DERR_BAD_NNODES, DERR_BAD_PAGE, DERR_BAD_PREFIX, DERR_BAD_DEPTH = (
     1, 2, 4, 8, 16, 32)
 DERR_BAD_TOKEN, DERR_BAD_PATH, DERR_BAD_UNIFORM = 64, 128, 256
@@ -44,6 +46,8 @@ SIGNATURES = {
     "jt_accept_workspace": (_c_size, [_c_int] * 3),
     "jt_accept": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp, _vp,
                            _vp, _vp, _vp, _vp, _c_size, _vp]),
+    "jt_accept_noalloc": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp,
+                                   _vp, _vp, _vp, _vp, _vp, _vp]),
     "jt_accept_margin": (_c_int, [_vp, _c_int, _c_int, _c_int, _c_int, _c_int, _vp, _vp, _vp, _vp,
                                   ctypes.c_double, ctypes.c_double, _vp, _vp, _vp, _vp, _vp,
                                   _c_size, _vp]),
@@ -227,6 +231,20 @@ def jt_accept(target_logits, depth_n: int, parent, token, depth, n_nodes, err=No
         _ptr(token), _ptr(depth), _ptr(n_nodes), _ptr(alen), _ptr(anodes), _ptr(bonus),
         _ptr(err), _ptr(ws), ws.numel(), _stream()))
     return alen, anodes, bonus
+
+
+def jt_accept_noalloc(target_logits, depth_n: int, parent, token, depth, n_nodes, accept_len,
+                      accept_nodes, bonus_token, err=None):
+    """jt_accept without a workspace (the library's static scratch instead);
+    the caller passes every output, so nothing is allocated here either."""
+    lib = load()
+    _cuda(target_logits, "target_logits")
+    b, T, V = target_logits.shape
+    _check("jt_accept_noalloc", lib.jt_accept_noalloc(
+        _ptr(target_logits), _dtype_code(target_logits), b, T, V, depth_n, _ptr(parent),
+        _ptr(token), _ptr(depth), _ptr(n_nodes), _ptr(accept_len), _ptr(accept_nodes),
+        _ptr(bonus_token), _ptr(err), _stream()))
+    return accept_len, accept_nodes, bonus_token
 
 
 def jt_accept_margin(target_logits, depth_n: int, parent, token, depth, n_nodes,

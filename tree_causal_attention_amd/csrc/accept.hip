@@ -20,6 +20,7 @@
 #include "jt_host.h"
 
 #include <algorithm>
+#include <mutex>
 
 namespace jt {
 
@@ -257,6 +258,36 @@ static void launch_argmax(const void* logits, int batch, int max_nodes, int voca
   hipLaunchKernelGGL((row_argmax<T, VEC>), dim3(p.chunks, max_nodes, batch), dim3(kArgmaxThreads),
                      0, stream, static_cast<const T*>(logits), n_nodes, max_nodes, vocab, p.chunks,
                      p.chunk_len, pv, pi, err);
+}
+
+// Scratch of the no-allocation entry point: the argmax partials live in this
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy until the process ends.  Host code never passes the array's name
+// to a kernel (on the host it is only a stand-in): the device address comes
+// from hipGetSymbolAddress, looked up once per device with that device
+// current, and is cached here.
+static __device__ __align__(256) unsigned char scratch[kAcceptScratchBytes];
+
+namespace {
+constexpr int kMaxScratchDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxScratchDevices] = {};
+}  // namespace
+
+hipError_t accept_scratch_address(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxScratchDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = p;
+  }
+  *out = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 hipError_t accept_launch(const void* logits, jt_dtype dt, int batch, int max_nodes, int vocab,

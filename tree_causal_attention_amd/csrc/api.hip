@@ -29,6 +29,7 @@ const char* jt_status_string(jt_status s) {
     case JT_ERR_UNSUPPORTED: return "unsupported configuration";
     case JT_ERR_WORKSPACE: return "workspace missing or too small";
     case JT_ERR_LAUNCH: return "kernel launch failed";
+    case JT_ERR_SCRATCH: return "inputs need more than the no-allocation entry point's scratch";
   }
   return "unknown status";
 }
@@ -188,6 +189,27 @@ jt_status jt_accept(const void* target_logits, jt_dtype dt, int batch, int max_n
   return accept_common(target_logits, dt, batch, max_nodes, vocab, depth_n, parent, token,
                        depth, n_nodes, accept_len, accept_nodes, bonus_token, err, workspace,
                        workspace_bytes, stream, 0, 0.0);
+}
+
+jt_status jt_accept_noalloc(const void* target_logits, jt_dtype dt, int batch, int max_nodes,
+                            int vocab, int depth_n, const int32_t* parent, const int32_t* token,
+                            const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
+                            int32_t* accept_nodes, int32_t* bonus_token, int32_t* err,
+                            void* stream) {
+  if (batch < 0 || max_nodes < 1 || vocab < 1 || depth_n < 1 || !valid_dtype(dt))
+    return JT_ERR_INVALID_ARG;
+  if (max_nodes > kMaxNodes || depth_n > kMaxDepth) return JT_ERR_UNSUPPORTED;
+  if (batch == 0) return JT_OK;
+  if (!target_logits || !parent || !token || !depth || !n_nodes || !accept_len ||
+      !accept_nodes || !bonus_token)
+    return JT_ERR_INVALID_ARG;
+  const size_t need = jt::accept_workspace_bytes(batch, max_nodes, vocab);
+  if (need > jt::kAcceptScratchBytes) return JT_ERR_SCRATCH;
+  void* scratch = nullptr;
+  if (jt::accept_scratch_address(&scratch) != hipSuccess) return JT_ERR_LAUNCH;
+  return launched(jt::accept_launch(target_logits, dt, batch, max_nodes, vocab, depth_n, parent,
+                                    token, depth, n_nodes, accept_len, accept_nodes, bonus_token,
+                                    err, scratch, static_cast<hipStream_t>(stream), 0, 0.0));
 }
 
 jt_status jt_accept_margin(const void* target_logits, jt_dtype dt, int batch, int max_nodes,

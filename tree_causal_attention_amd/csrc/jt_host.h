@@ -51,6 +51,9 @@ hipError_t tree_attention_launch(const AttnShape& s, const void* q, const void* 
 
 // accept.hip
 size_t accept_workspace_bytes(int batch, int max_nodes, int vocab);
+// no-allocation acceptance: a static device array replaces the workspace
+constexpr size_t kAcceptScratchBytes = JT_ACCEPT_SCRATCH_BYTES;
+hipError_t accept_scratch_address(void** out);  // this device's copy of the array
 hipError_t accept_launch(const void* logits, jt_dtype dt, int batch, int max_nodes, int vocab,
                          int depth_n, const int32_t* parent, const int32_t* token,
                          const int32_t* depth, const int32_t* n_nodes, int32_t* accept_len,
