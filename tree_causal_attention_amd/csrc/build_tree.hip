@@ -9,14 +9,17 @@
 //   complete tree, because a child never precedes its parent.  It is computed
 //   level by level: level d keeps the best cap_d = min(W^d, B-d+1) children of
 //   level d-1 (a depth-d node in the final tree is preceded by its d-1
-//   ancestors, so no deeper position can be selected); the W candidate columns
-//   of a level are each sorted, so the level is their merge (merge path), and
-//   the sorted levels are merged the same way into the global pop order.  Once
-//   B kept nodes score at or above some kept score, that score bounds the
-//   selection from below and later levels keep only children at or above it.
-//   All
-//   arithmetic on scores is fp64 and identical to a sequential evaluation
-//   except the per-depth log-sum-exp, whose summation order differs.
+//   ancestors, so no deeper position can be selected).  Every position is
+//   found by counting: the W candidate columns of a level are each sorted, so
+//   an entry's rank in the level is its own position plus one binary search
+//   per other column; its node index is its level position plus one binary
+//   search per other sorted level.  Each thread owns one entry and runs its
+//   searches in lockstep, so a level costs one round of searches and no merge
+//   passes.  Once B kept nodes score at or above some kept score, that score
+//   bounds the selection from below and later levels keep only children at or
+//   above it.  All arithmetic on scores is fp64 and identical to a sequential
+//   evaluation except the per-depth log-sum-exp, whose summation order
+//   differs.
 // tree_select_seq (the variants): a literal best-first search, described below.
 #include "jt_device.h"
 #include "jt_host.h"
@@ -39,14 +42,16 @@ __host__ __device__ inline int level_cap(int d, int width, int budget) {
   return c < 0 ? 0 : static_cast<int>(c);
 }
 
+constexpr int kSelectMaxDepth = 64;
+
 struct SelectLayout {
-  int tot;         // sum of level capacities
-  int capmax;      // max level capacity
-  int wp;          // power of two >= W (lists merged per level)
-  int np;          // power of two >= N (lists merged across levels)
-  int mstride;     // list stride of the phase-3 merge buffers (>= 1)
-  size_t off_S, off_lse, off_cval, off_ctok, off_loff, off_lcnt, off_rawa, off_rawb;
-  size_t off_score, off_info, off_gidx, off_ms0, off_ms1, off_mi0, off_mi1, off_len, bytes;
+  int tot;     // sum of level capacities
+  int capmax;  // max level capacity
+  int loff[kSelectMaxDepth + 2];  // level d starts at loff[d] in the level arrays
+  int coff[17];                   // column k of a level's candidates starts at coff[k]
+  size_t off_S, off_lse, off_cval, off_ctok, off_loff, off_lcnt, off_npart, off_coff, off_wlen,
+      off_rawa, off_rawb;
+  size_t off_canda, off_candb, off_score, off_info, off_gidx, off_order, off_ga, off_gb, bytes;
 };
 
 inline SelectLayout select_layout(int depth_n, int width, int budget, int wmax) {
@@ -55,33 +60,39 @@ inline SelectLayout select_layout(int depth_n, int width, int budget, int wmax) 
   L.capmax = 1;
   for (int d = 1; d <= depth_n; ++d) {
     const int c = level_cap(d, width, budget);
+    L.loff[d] = L.tot;
     L.tot += c;
     L.capmax = std::max(L.capmax, c);
   }
-  L.wp = 1;
-  while (L.wp < width) L.wp <<= 1;
-  L.np = 1;
-  while (L.np < depth_n) L.np <<= 1;
-  L.mstride = std::max(1, budget);
-  const size_t mcount = std::max(static_cast<size_t>(L.wp) * L.capmax,
-                                 static_cast<size_t>(L.np) * L.mstride);
+  L.loff[0] = 0;
+  L.loff[depth_n + 1] = L.tot;
+  // column k of a level never holds more than capmax / (k + 1) candidates
+  int cc = 0;
+  for (int k = 0; k < wmax; ++k) {
+    L.coff[k] = cc;
+    cc += std::max(1, L.capmax / (k + 1));
+  }
+  L.coff[wmax] = cc;
   size_t o = 0;
   auto take = [&](size_t n, size_t align) { o = (o + align - 1) / align * align; size_t r = o; o += n; return r; };
   L.off_S = take(sizeof(double) * (depth_n + 1), 8);
   L.off_lse = take(sizeof(double) * depth_n, 8);
   L.off_rawa = take(sizeof(double) * L.capmax, 8);
   L.off_rawb = take(sizeof(double) * L.capmax, 8);
+  L.off_canda = take(sizeof(double) * cc, 8);
+  L.off_candb = take(sizeof(double) * cc, 8);
   L.off_score = take(sizeof(double) * std::max(1, L.tot), 8);
-  L.off_ms0 = take(sizeof(double) * L.wp * L.capmax, 8);
-  L.off_ms1 = take(sizeof(double) * L.wp * L.capmax, 8);
+  L.off_ga = take(sizeof(double) * std::max(1, budget), 8);
+  L.off_gb = take(sizeof(double) * std::max(1, budget), 8);
   L.off_cval = take(sizeof(float) * depth_n * wmax, 4);
   L.off_ctok = take(sizeof(int) * depth_n * wmax, 4);
   L.off_loff = take(sizeof(int) * (depth_n + 2), 4);
   L.off_lcnt = take(sizeof(int) * (depth_n + 2), 4);
+  L.off_npart = take(sizeof(int) * (depth_n + 2), 4);
+  L.off_coff = take(sizeof(int) * 17, 4);
+  L.off_wlen = take(sizeof(int) * (kSelectThreads / kWave) * wmax, 4);
   L.off_info = take(sizeof(uint32_t) * std::max(1, L.tot), 4);
-  L.off_mi0 = take(sizeof(uint32_t) * mcount, 4);
-  L.off_mi1 = take(sizeof(uint32_t) * mcount, 4);
-  L.off_len = take(sizeof(int) * 2 * std::max(L.wp, L.np), 4);
+  L.off_order = take(sizeof(uint32_t) * std::max(1, budget), 4);
   L.off_gidx = take(sizeof(uint16_t) * std::max(1, L.tot), 2);
   L.bytes = (o + 15) / 16 * 16;
   return L;
@@ -105,24 +116,27 @@ __device__ __noinline__ bool precedes_tied(const double* score, const uint32_t* 
   }
 }
 
+// A value every lane of the wave holds alike (read from LDS after a barrier),
+// moved to scalar registers.
+__device__ __forceinline__ int uniform(int v) { return __builtin_amdgcn_readfirstlane(v); }
+__device__ __forceinline__ float uniform(float v) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ double uniform(double v) {
+  const int2 b = __builtin_bit_cast(int2, v);
+  return __builtin_bit_cast(double, make_int2(__builtin_amdgcn_readfirstlane(b.x),
+                                              __builtin_amdgcn_readfirstlane(b.y)));
+}
+
+// Number of binary-search steps over n entries: ceil(log2(n + 1)).
+__device__ __forceinline__ int bitwidth(int n) { return n > 0 ? 32 - __clz(n) : 0; }
+
 // Same-level order of two candidates (score, info = parent position | rank << 16).
 __device__ __forceinline__ bool precedes_level(double sa, uint32_t ia, double sb, uint32_t ib) {
   if (sa != sb) return sa > sb;
   const uint32_t pa = ia & 0xFFFFu, pb = ib & 0xFFFFu;
   if (pa != pb) return pa < pb;
   return (ia >> 16) < (ib >> 16);
-}
-
-// Merge path: number of elements of A among the first o outputs of merge(A, B)
-// under a strict order (A[i-1] precedes B[o-i] holds exactly for i <= answer).
-template <typename Prec>
-__device__ __forceinline__ int co_rank(int o, int la, int lb, Prec prec_ab) {
-  int lo = max(0, o - lb), hi = min(o, la);
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (prec_ab(mid - 1, o - mid)) lo = mid; else hi = mid - 1;
-  }
-  return lo;
 }
 
 // Wave argmax of (value, id) under `better`, through DPP lane moves into lane
@@ -215,14 +229,100 @@ __device__ void merge_depth_partials(const float* __restrict__ part_max,
   }
 }
 
+struct RankArgs {
+  const double* cand;    // this level's columns (column k at coff[k])
+  double* cand_next;     // the next level's columns
+  const double* raw_prev;
+  double* raw_cur;
+  double* score;         // this level's sorted scores
+  uint32_t* info;        // parent position | rank << 16
+  const int* coff;
+  const int* wlen;        // this wave's copy of the column lengths
+  const float* cv;        // this level's draft values (top-W log-probs before normalising)
+  const float* cvn;       // the next level's
+  int width, cap, cap_n;  // cap_n: the next level's capacity (0: no next level)
+  double s_next;          // S of the next level
+  int threads;
+};
+
+// Rank every candidate of a level (see phase 2 below) and place the kept
+// ones.  Candidate c is served by lpc = WMAX / (KC * NG) adjacent lanes; lane
+// `sub` searches the columns sub, sub + lpc, ... (KC * NG of them), KC at a
+// time in lockstep.
+template <int WMAX, int KC, int NG>
+__device__ __forceinline__ void rank_entries(const RankArgs& a, const int (&lens)[WMAX],
+                                             int items, int csteps) {
+  if constexpr (KC * NG > WMAX) {
+    return;
+  } else {
+    constexpr int LPC = WMAX / (KC * NG);
+    for (int it = threadIdx.x; it < items; it += a.threads) {
+      const int c = it / LPC, sub = it % LPC;
+      int k = 0, p = c;
+#pragma unroll
+      for (int kk = 0; kk + 1 < WMAX; ++kk)
+        if (k == kk && p >= lens[kk]) { p -= lens[kk]; k = kk + 1; }
+      const double sc = a.cand[a.coff[k] + p];
+      int cnt = 0;
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        int lo[KC], hi[KC], base[KC], pt[KC];
+#pragma unroll
+        for (int j = 0; j < KC; ++j) {
+          const int k2 = sub + (g * KC + j) * LPC;
+          lo[j] = 0;
+          hi[j] = k2 != k ? a.wlen[k2] : 0;
+          base[j] = a.coff[k2];
+          pt[j] = p + (k2 < k ? 1 : 0);  // on equal scores, (q, k2) precedes iff q < pt
+        }
+        for (int step = 0; step < csteps; ++step) {
+          double v[KC];
+          // mid <= hi <= the column's capacity: at worst the first slot past
+          // the column, still inside the buffers, and then unused
+#pragma unroll
+          for (int j = 0; j < KC; ++j) v[j] = a.cand[base[j] + ((lo[j] + hi[j]) >> 1)];
+#pragma unroll
+          for (int j = 0; j < KC; ++j) {
+            const int mid = (lo[j] + hi[j]) >> 1;
+            const int pr = static_cast<int>(v[j] > sc) |
+                           (static_cast<int>(v[j] == sc) & static_cast<int>(mid < pt[j]));
+            const int act = static_cast<int>(lo[j] < hi[j]);
+            lo[j] = (act & pr) ? mid + 1 : lo[j];
+            hi[j] = (act & (pr ^ 1)) ? mid : hi[j];
+          }
+        }
+#pragma unroll
+        for (int j = 0; j < KC; ++j) cnt += lo[j];
+      }
+#pragma unroll
+      for (int o = 1; o < LPC; o <<= 1) cnt += shfl_xor(cnt, o);
+      const int rank = p + cnt;
+      if (rank < a.cap) {
+        const double raw = a.raw_prev[p] + static_cast<double>(a.cv[k]);
+        if (sub == 0) {
+          a.score[rank] = sc;
+          a.info[rank] = static_cast<uint32_t>(p) | (static_cast<uint32_t>(k) << 16);
+          a.raw_cur[rank] = raw;
+        }
+        // this entry's children: the next level's columns
+#pragma unroll
+        for (int j = 0; j < KC * NG; ++j) {
+          const int k2 = sub + j * LPC;
+          if (k2 < a.width && (rank + 1) * (k2 + 1) <= a.cap_n)  // rank < cap_n / (k2 + 1)
+            a.cand_next[a.coff[k2] + rank] = (raw + static_cast<double>(a.cvn[k2])) - a.s_next;
+        }
+      }
+    }
+  }
+}
+
 // One workgroup per sequence.
 //  phase 1: per depth, merge the chunk partials (lse, top-W).
-//  phase 2: per level d, the W candidate columns (children of the sorted level
-//    d-1 by rank k; each column sorted, pruned to the first cap_d/(k+1) rows)
-//    are merged pairwise (merge path, log2 W rounds) into the sorted level,
-//    truncated to cap_d.
-//  phase 3: the sorted levels are merged pairwise (log2 N rounds, truncated to
-//    B) under the global key; the merged position is the node index.
+//  phase 2: per level d, rank every candidate of the W columns (children of
+//    the sorted level d-1 by rank k; column k cut to its first cap_d/(k+1)
+//    rows) by counting; keep ranks below cap_d; update the lower bound tau.
+//  phase 3: rank every kept entry across the levels under the global key; the
+//    rank + 1 is the node index.
 //  phase 4: write parent/token/depth/score in node order.
 template <int WMAX>
 __global__ __launch_bounds__(kSelectThreads) void tree_select(
@@ -236,202 +336,288 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   double* lse = reinterpret_cast<double*>(smem + L.off_lse);
   double* raw_a = reinterpret_cast<double*>(smem + L.off_rawa);
   double* raw_b = reinterpret_cast<double*>(smem + L.off_rawb);
+  double* cand_a = reinterpret_cast<double*>(smem + L.off_canda);
+  double* cand_b = reinterpret_cast<double*>(smem + L.off_candb);
   double* lv_score = reinterpret_cast<double*>(smem + L.off_score);
-  double* ms[2] = {reinterpret_cast<double*>(smem + L.off_ms0),
-                   reinterpret_cast<double*>(smem + L.off_ms1)};
+  double* g_a = reinterpret_cast<double*>(smem + L.off_ga);
+  double* g_b = reinterpret_cast<double*>(smem + L.off_gb);
   float* cval = reinterpret_cast<float*>(smem + L.off_cval);
   int* ctok = reinterpret_cast<int*>(smem + L.off_ctok);
   int* loff = reinterpret_cast<int*>(smem + L.off_loff);
   int* lcnt = reinterpret_cast<int*>(smem + L.off_lcnt);
+  int* npart = reinterpret_cast<int*>(smem + L.off_npart);
+  int* coff = reinterpret_cast<int*>(smem + L.off_coff);  // column offsets (LDS copy)
+  int* wlen_all = reinterpret_cast<int*>(smem + L.off_wlen);
   uint32_t* lv_info = reinterpret_cast<uint32_t*>(smem + L.off_info);
-  uint32_t* mi[2] = {reinterpret_cast<uint32_t*>(smem + L.off_mi0),
-                     reinterpret_cast<uint32_t*>(smem + L.off_mi1)};
-  int* lens = reinterpret_cast<int*>(smem + L.off_len);  // [2][max(wp, np)]
+  uint32_t* order = reinterpret_cast<uint32_t*>(smem + L.off_order);  // node - 1 -> level << 16 | pos
   uint16_t* lv_gidx = reinterpret_cast<uint16_t*>(smem + L.off_gidx);
-  const int lstride = max(L.wp, L.np);
 
   const int seq = blockIdx.x;
   const int tid = threadIdx.x;
+  const int lane = tid % kWave;
   const int nwaves = kSelectThreads / kWave;
 
   // ---- phase 1: merge the chunk partials of every depth
   merge_depth_partials<WMAX>(part_max, part_sum, nullptr, part_val, part_idx, chunks, depth_n,
                              width, seq, lse, nullptr, cval, ctok, err, nwaves);
   __syncthreads();
-  if (tid == 0) {
-    S[0] = 0.0;
-    for (int d = 0; d < depth_n; ++d) S[d + 1] = S[d] + lse[d];
-    int o = 0;
-    loff[0] = 0;
-    lcnt[0] = 1;
-    for (int d = 1; d <= depth_n; ++d) { loff[d] = o; o += level_cap(d, width, budget); }
-    loff[depth_n + 1] = o;
-    raw_a[0] = 0.0;
+  if (tid <= depth_n + 1) {
+    // S_d = lse_0 + ... + lse_{d-1}, summed in that order
+    double sd = 0.0;
+    for (int j = 0; j < depth_n; ++j) {
+      const double v = lse[j];
+      if (j < tid) sd += v;
+    }
+    if (tid <= depth_n) S[tid] = sd;
+    loff[tid] = L.loff[tid];
   }
+  if (tid <= WMAX) coff[tid] = L.coff[tid];
+  if (tid == 0) lcnt[0] = 1;
   for (int x = tid; x < L.tot; x += kSelectThreads) lv_gidx[x] = 0xFFFF;
   __syncthreads();
 
-  // ---- phase 2: level by level, the best cap_d children in key order
-  double* raw_prev = raw_a;
-  double* raw_cur = raw_b;
-  int m_prev = 1;
-  int last_level = 0;
-  // A lower bound tau of the B-th best score of the tree: any score t such
-  // that B kept nodes score >= t.  For the entries t of the newest level the
-  // count is (position + 1) plus, per earlier level, the entries >= t (binary
-  // search in its sorted list); tau is the largest entry whose count reaches
-  // B.  Children scoring below tau can never be selected, and since a
-  // column's scores fall with the parent position they form a suffix that is
-  // cut off.  The kept lists stay prefixes of the uncut ones, so the result
-  // is unchanged; deep levels usually empty out and the loop ends early.
-  __shared__ int s_istar;
+  // ---- phase 2: level by level, the best children in key order.
+  // The candidates of level d form W columns: column k holds the children
+  // (p, k) of the first len_k parents of the sorted level d-1, with score
+  // (raw_p + cval_k) - S_d (raw_p: the parent's cumulative draft log-prob
+  // before normalising); a column is that sorted level shifted by one
+  // constant, so it is sorted itself.  The threads that place an entry of
+  // level d-1 also write its children's scores into the columns of level d.
+  // An entry's rank in its level is its position p plus, for every other
+  // column, the number of that column's entries that precede it, found by
+  // binary search; the searches of one entry are spread over `lpc` adjacent
+  // lanes (each runs its columns in lockstep, branch-free: one round trip to
+  // LDS a step) and summed by lane shuffles.  Entries ranked below the level's
+  // capacity are kept, written at their rank.
+  //
+  // tau is a lower bound of the B-th best score tau* of the tree.  Children
+  // scoring below it can never be selected; in every column they form a
+  // suffix, cut off before ranking, and they trail every entry >= tau in the
+  // level order, so the kept levels stay prefixes of the uncut ones and the
+  // result is unchanged.
+  //
+  // Two passes.  Pass 1 keeps at most T entries a level (the exact top T of
+  // each level: the best T children of a level are children of the best T
+  // parents).  Its kept entries are real nodes, so the B-th best of them,
+  // tau1, is a lower bound of tau*.  It is found by merging each level into
+  // G, the sorted top-B scores kept so far: one wave merges level d-1 while
+  // the others rank level d, so tau lags a level behind and tightens as it
+  // goes; the round after the last level merges it too.  If every level that
+  // pass 1 truncated ends below tau1, no node scoring >= tau1 was left out,
+  // so tau1 = tau* and the pass-1 levels hold the whole selection.  Otherwise
+  // pass 2 rebuilds the levels at their full capacity, cut at tau1 from the
+  // first level on.
+  const int t1 = max(64, 2 * ((budget + depth_n - 1) / depth_n));
   double tau = -INFINITY;
-  int prev_cnt = 0;
-  for (int d = 1; d <= depth_n; ++d) {
-    const int cap = level_cap(d, width, budget);
-    if (cap <= 0 || m_prev == 0) break;
-    const double Sd = S[d];
-    // column k holds children (p, k) of the first len_k parents
-    if (tid < L.wp) {
-      int lk = tid < width ? min(m_prev, cap / (tid + 1)) : 0;
-      if (tau != -INFINITY && lk > 0) {
-        const double c = static_cast<double>(cval[(d - 1) * WMAX + tid]);
-        int lo = 0, hi = lk;  // first parent whose child scores below tau
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if ((raw_prev[mid] + c) - Sd >= tau) lo = mid + 1; else hi = mid;
+  int last_level = 0;
+  for (int pass = 1; pass <= 2; ++pass) {
+    const bool merge_g = pass == 1;
+    const int tmax = pass == 1 ? t1 : budget;
+    const int rank_threads = merge_g ? kSelectThreads - kWave : kSelectThreads;
+    double* raw_prev = raw_a;
+    double* raw_cur = raw_b;
+    double* cand_cur = cand_a;
+    double* cand_nxt = cand_b;
+    double* g_old = g_a;
+    double* g_new = g_b;
+    // level 1's columns: the children of the root (raw 0)
+    if (tid < width && tid < WMAX) {
+      const int c1 = min(loff[2] - loff[1], tmax);
+      if (tid < c1) cand_a[coff[tid]] = (0.0 + static_cast<double>(cval[tid])) - S[1];
+    }
+    if (tid == 0) raw_a[0] = 0.0;
+    __syncthreads();
+    int m_prev = 1, gn = 0;
+    bool complete = true;  // pass 1: no truncated level ends at or above tau1 (checked below)
+    last_level = 0;
+    for (int d = 1;; ++d) {
+      // level capacities are the differences of the level offsets
+      const int cap_full = d <= depth_n ? uniform(loff[d + 1] - loff[d]) : 0;
+      const int cap = min(cap_full, tmax);
+      const bool grow = cap > 0 && m_prev > 0;
+      // column lengths, cut at tau: lane k of every wave searches column k
+      int myl = 0;
+      if (grow && lane < width && lane < WMAX) {
+        int hi = min(m_prev, cap / (lane + 1));
+        if (tau != -INFINITY) {
+          const double* col = cand_cur + coff[lane];
+          int lo = 0;
+          while (lo < hi) {
+            const int mid = (lo + hi) >> 1;
+            if (col[mid] >= tau) lo = mid + 1; else hi = mid;
+          }
         }
-        lk = lo;
+        myl = hi;
       }
-      lens[tid] = lk;
-    }
-    __syncthreads();
-    // columns: list k at ms/mi[0] + k * cap
-    for (int idx = tid; idx < L.wp * cap; idx += kSelectThreads) {
-      const int k = idx / cap, p = idx % cap;
-      if (p < lens[k]) {
-        ms[0][idx] = (raw_prev[p] + static_cast<double>(cval[(d - 1) * WMAX + k])) - Sd;
-        mi[0][idx] = static_cast<uint32_t>(p) | (static_cast<uint32_t>(k) << 16);
+      // every wave keeps its own LDS copy of the column lengths (read by lane)
+      if (lane < WMAX) wlen_all[(tid / kWave) * WMAX + lane] = myl;
+      int lens[WMAX];
+      int total_a = 0;
+#pragma unroll
+      for (int k = 0; k < WMAX; ++k) {
+        lens[k] = __builtin_amdgcn_readlane(myl, k);
+        total_a += lens[k];
       }
-    }
-    __syncthreads();
-    int src = 0;
-    for (int lists = L.wp; lists > 1; lists >>= 1) {
-      const int pairs = lists >> 1;
-      const int* lsrc = lens + src * lstride;
-      int* ldst = lens + (src ^ 1) * lstride;
-      for (int idx = tid; idx < pairs * cap; idx += kSelectThreads) {
-        const int q = idx / cap, o = idx % cap;
-        const int la = lsrc[2 * q], lb = lsrc[2 * q + 1];
-        if (o >= min(cap, la + lb)) continue;
-        const double* As = ms[src] + (2 * q) * cap;
-        const uint32_t* Ai = mi[src] + (2 * q) * cap;
-        const double* Bs = As + cap;
-        const uint32_t* Bi = Ai + cap;
-        const int i = co_rank(o, la, lb, [&](int ia, int jb) {
-          return precedes_level(As[ia], Ai[ia], Bs[jb], Bi[jb]);
-        });
-        const int j = o - i;
-        const bool take_a = i < la && (j >= lb || precedes_level(As[i], Ai[i], Bs[j], Bi[j]));
-        ms[src ^ 1][q * cap + o] = take_a ? As[i] : Bs[j];
-        mi[src ^ 1][q * cap + o] = take_a ? Ai[i] : Bi[j];
-      }
-      if (tid < pairs) ldst[tid] = min(cap, lsrc[2 * tid] + lsrc[2 * tid + 1]);
-      __syncthreads();
-      src ^= 1;
-    }
-    const int m_d = lens[src * lstride];
-    for (int o = tid; o < m_d; o += kSelectThreads) {
-      const uint32_t inf = mi[src][o];
-      lv_score[loff[d] + o] = ms[src][o];
-      lv_info[loff[d] + o] = inf;
-      raw_cur[o] = raw_prev[inf & 0xFFFFu] + static_cast<double>(cval[(d - 1) * WMAX + (inf >> 16)]);
-    }
-    if (tid == 0) {
-      lcnt[d] = m_d;
-      s_istar = INT_MAX;
-    }
-    __syncthreads();
-    if (prev_cnt + m_d >= budget) {
-      // count[i] = i + 1 + sum over earlier levels of their entries >= the
-      // i-th entry; one (entry, earlier level) binary search per thread step,
-      // summed by LDS atomics (the merge buffers are free until the next level)
-      int* cnt = reinterpret_cast<int*>(mi[0]);
-      for (int i = tid; i < m_d; i += kSelectThreads) cnt[i] = i + 1;
-      __syncthreads();
-      for (int x = tid; x < m_d * (d - 1); x += kSelectThreads) {
-        const int i = x % m_d, dd = 1 + x / m_d;
-        const double t = lv_score[loff[d] + i];
-        const double* ls = lv_score + loff[dd];
-        int lo = 0, hi = lcnt[dd];  // entries >= t form a prefix
-        while (lo < hi) {
-          const int mid = (lo + hi) >> 1;
-          if (ls[mid] >= t) lo = mid + 1; else hi = mid;
+      const int m_d = min(cap, total_a);
+      const int cap_n = (grow && d < depth_n) ? min(uniform(loff[d + 2] - loff[d + 1]), tmax) : 0;
+      const double Sn = cap_n > 0 ? uniform(S[d + 1]) : 0.0;
+      // lanes per entry: as many as keep every entry within one round
+      int lpc = WMAX;
+      while (lpc > 1 && total_a * lpc > rank_threads) lpc >>= 1;
+      const int cpl = WMAX / lpc;  // columns per lane
+      const int items = total_a * lpc;
+      const int csteps = bitwidth(m_prev);
+      if (tid < rank_threads) {
+        const RankArgs ra{cand_cur, cand_nxt, raw_prev, raw_cur, lv_score + loff[d],
+                          lv_info + loff[d], coff, wlen_all + (tid / kWave) * WMAX,
+                          cval + (d - 1) * WMAX, cap_n > 0 ? cval + d * WMAX : cval,
+                          width, cap, cap_n, Sn, rank_threads};
+        switch (cpl) {
+          case 1: rank_entries<WMAX, 1, 1>(ra, lens, items, csteps); break;
+          case 2: rank_entries<WMAX, 2, 1>(ra, lens, items, csteps); break;
+          case 4: rank_entries<WMAX, 4, 1>(ra, lens, items, csteps); break;
+          case 8: rank_entries<WMAX, 4, 2>(ra, lens, items, csteps); break;
+          default: rank_entries<WMAX, 4, 4>(ra, lens, items, csteps); break;
         }
-        if (lo > 0) atomicAdd(&cnt[i], lo);
+      } else if (merge_g && d >= 2) {
+        // the last wave merges level d-1 into G (stable: G first on equal
+        // scores), each lane a run of consecutive outputs found by merge path
+        const int mb = m_prev;
+        const double* lvl = lv_score + loff[d - 1];
+        const int n_out = min(budget, gn + mb);
+        const int per = (n_out + kWave - 1) / kWave;
+        const int o0 = min(lane * per, n_out), o1 = min(o0 + per, n_out);
+        if (o0 < o1) {
+          // i = number of G entries among the first o0 outputs
+          int lo = max(0, o0 - mb), hi = min(o0, gn);
+          while (lo < hi) {
+            const int mid = (lo + hi + 1) >> 1;  // does G[mid-1] come before L[o0-mid]?
+            if (g_old[mid - 1] >= lvl[o0 - mid]) lo = mid; else hi = mid - 1;
+          }
+          int i = lo, j = o0 - lo;
+          for (int o = o0; o < o1; ++o) {
+            const bool take_g = i < gn && (j >= mb || g_old[i] >= lvl[j]);
+            g_new[o] = take_g ? g_old[i] : lvl[j];
+            i += take_g ? 1 : 0;
+            j += take_g ? 0 : 1;
+          }
+        }
       }
       __syncthreads();
-      for (int i = tid; i < m_d; i += kSelectThreads)
-        if (cnt[i] >= budget) atomicMin(&s_istar, i);
-      __syncthreads();
-      if (s_istar != INT_MAX) tau = fmax(tau, lv_score[loff[d] + s_istar]);
+      if (merge_g && d >= 2 && m_prev > 0) {
+        gn = min(budget, gn + m_prev);
+        double* g = g_old; g_old = g_new; g_new = g;
+        if (gn >= budget && budget > 0) tau = uniform(g_old[budget - 1]);
+      }
+      if (!grow) break;
+      if (tid == 0) lcnt[d] = m_d;
+      if (cap < cap_full && m_d == cap) complete = false;  // truncated: checked against tau1
+      double* r = raw_prev; raw_prev = raw_cur; raw_cur = r;
+      double* cn = cand_cur; cand_cur = cand_nxt; cand_nxt = cn;
+      m_prev = m_d;
+      last_level = d;
     }
-    prev_cnt += m_d;
-    double* t = raw_prev; raw_prev = raw_cur; raw_cur = t;
-    m_prev = m_d;
-    last_level = d;
+    if (pass == 2 || complete) break;
+    // a full truncated level is fine when its last entry scores below tau1
+    complete = true;
+    for (int d0 = 1; d0 <= last_level; d0 += kWave) {
+      const int d = d0 + lane;  // one level a lane
+      bool bad = false;
+      if (d <= last_level) {
+        const int m_d = lcnt[d];
+        bad = t1 < loff[d + 1] - loff[d] && m_d == t1 && !(lv_score[loff[d] + m_d - 1] < tau);
+      }
+      if (__ballot(bad) != 0) complete = false;
+    }
+    if (complete) break;
+    __syncthreads();  // pass 2 overwrites the levels every thread has just read
   }
   if (tid == 0)
     for (int d = last_level + 1; d <= depth_n; ++d) lcnt[d] = 0;
+  // the entries scoring at least tau: a prefix of every level
+  if (tid >= 1 && tid <= last_level) {
+    const double* ls = lv_score + loff[tid];
+    const int n = lcnt[tid];
+    int lo = 0, hi = n;
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (ls[mid] >= tau) lo = mid + 1; else hi = mid;
+    }
+    npart[tid] = lo;
+  }
   __syncthreads();
 
-  // ---- phase 3: merge the sorted levels into the global order
-  const int B = L.mstride;
-  for (int idx = tid; idx < L.np * B; idx += kSelectThreads) {
-    const int l = idx / B, o = idx % B;
-    if (l < depth_n && o < lcnt[l + 1])
-      mi[0][idx] = (static_cast<uint32_t>(l + 1) << 16) | static_cast<uint32_t>(o);
+  // ---- phase 3: the global order.  A participant's node index is 1 + the
+  // number of participants that precede it: its position in its own level
+  // plus, for every other level, a binary search under the global key (ties
+  // between levels compare the parents up the two paths).  The searches of
+  // one participant are spread over lpc adjacent lanes, 4 levels at a time in
+  // lockstep, and summed by lane shuffles.  Entries below tau trail all
+  // participants and are left out.
+  int tot_part = 0, maxpart = 0;
+  for (int d = 1; d <= last_level; ++d) {
+    const int n = npart[d];
+    tot_part += n;
+    maxpart = max(maxpart, n);
   }
-  if (tid < L.np) lens[tid] = tid < depth_n ? min(B, lcnt[tid + 1]) : 0;
-  __syncthreads();
-  auto prec_cross = [&](uint32_t ra, uint32_t rb) {
-    const int da = static_cast<int>(ra >> 16), ia = static_cast<int>(ra & 0xFFFFu);
-    const int db = static_cast<int>(rb >> 16), ib = static_cast<int>(rb & 0xFFFFu);
-    const double sa = lv_score[loff[da] + ia], sb = lv_score[loff[db] + ib];
-    if (sa != sb) return sa > sb;
-    return precedes_tied(lv_score, lv_info, loff, da, ia, db, ib);
-  };
-  int src = 0;
-  for (int lists = L.np; lists > 1; lists >>= 1) {
-    const int pairs = lists >> 1;
-    const int* lsrc = lens + src * lstride;
-    int* ldst = lens + (src ^ 1) * lstride;
-    for (int idx = tid; idx < pairs * B; idx += kSelectThreads) {
-      const int q = idx / B, o = idx % B;
-      const int la = lsrc[2 * q], lb = lsrc[2 * q + 1];
-      if (o >= min(B, la + lb)) continue;
-      const uint32_t* A = mi[src] + (2 * q) * B;
-      const uint32_t* Bv = A + B;
-      const int i = co_rank(o, la, lb, [&](int ia, int jb) { return prec_cross(A[ia], Bv[jb]); });
-      const int j = o - i;
-      const bool take_a = i < la && (j >= lb || prec_cross(A[i], Bv[j]));
-      mi[src ^ 1][q * B + o] = take_a ? A[i] : Bv[j];
+  tot_part = uniform(tot_part);
+  maxpart = uniform(maxpart);
+  int lpc = 16, lpc_log = 4;
+  while (lpc > 1 && (tot_part * lpc > kSelectThreads || lpc / 2 >= last_level)) {
+    lpc >>= 1;
+    --lpc_log;
+  }
+  const int psteps = bitwidth(maxpart);
+  for (int it = tid; it < tot_part * lpc; it += kSelectThreads) {
+    const int sub = it & (lpc - 1);
+    int d = 1, i = it >> lpc_log;
+    while (i >= npart[d]) { i -= npart[d]; ++d; }
+    const double sb = lv_score[loff[d] + i];
+    int cnt = 0;
+    for (int dd0 = 1 + sub; dd0 <= last_level; dd0 += 4 * lpc) {
+      int lo[4], hi[4], base[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int dd = dd0 + u * lpc;
+        const bool ok = dd <= last_level && dd != d;
+        lo[u] = 0;
+        hi[u] = ok ? npart[dd] : 0;
+        base[u] = ok ? loff[dd] : 0;
+      }
+      for (int step = 0; step < psteps; ++step) {
+        double v[4];
+        // mid <= hi <= the level's length: at worst one slot past it, still
+        // inside LDS, and then unused
+#pragma unroll
+        for (int u = 0; u < 4; ++u) v[u] = lv_score[base[u] + ((lo[u] + hi[u]) >> 1)];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int mid = (lo[u] + hi[u]) >> 1;
+          const bool act = lo[u] < hi[u];
+          bool pr = v[u] > sb;
+          if (act && v[u] == sb)
+            pr = precedes_tied(lv_score, lv_info, loff, dd0 + u * lpc, mid, d, i);
+          lo[u] = (act && pr) ? mid + 1 : lo[u];
+          hi[u] = (act && !pr) ? mid : hi[u];
+        }
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) cnt += lo[u];
     }
-    if (tid < pairs) ldst[tid] = min(B, lsrc[2 * tid] + lsrc[2 * tid + 1]);
-    __syncthreads();
-    src ^= 1;
+    for (int o = 1; o < lpc; o <<= 1) cnt += shfl_xor(cnt, o);
+    const int rank = i + cnt;
+    if (sub == 0 && rank < budget) {
+      order[rank] = (static_cast<uint32_t>(d) << 16) | static_cast<uint32_t>(i);
+      lv_gidx[loff[d] + i] = static_cast<uint16_t>(rank + 1);
+    }
   }
-  const int n_sel = min(budget, lens[src * lstride]);
-  for (int o = tid; o < n_sel; o += kSelectThreads) {
-    const uint32_t r = mi[src][o];
-    lv_gidx[loff[r >> 16] + (r & 0xFFFFu)] = static_cast<uint16_t>(o + 1);
-  }
+  const int n_sel = min(budget, tot_part);
   __syncthreads();
 
   // ---- phase 4: write the tree in node-index order
   const size_t base = static_cast<size_t>(seq) * (budget + 1);
   for (int o = tid; o < n_sel; o += kSelectThreads) {
-    const uint32_t r = mi[src][o];
+    const uint32_t r = order[o];
     const int d = static_cast<int>(r >> 16), i = static_cast<int>(r & 0xFFFFu);
     const int idx = loff[d] + i;
     const int g = o + 1;
