@@ -50,8 +50,9 @@ struct SelectLayout {
   int loff[kSelectMaxDepth + 2];  // level d starts at loff[d] in the level arrays
   int coff[17];                   // column k of a level's candidates starts at coff[k]
   size_t off_S, off_lse, off_cval, off_ctok, off_loff, off_lcnt, off_npart, off_coff, off_wlen,
-      off_rawa, off_rawb;
-  size_t off_canda, off_candb, off_score, off_info, off_gidx, off_order, off_ga, off_gb, bytes;
+      off_cut, off_rawa, off_rawb;
+  size_t off_canda, off_candb, off_score, off_info, off_gidx, off_order, off_ga, off_gb, off_gida,
+      off_gidb, bytes;
 };
 
 inline SelectLayout select_layout(int depth_n, int width, int budget, int wmax) {
@@ -91,8 +92,11 @@ inline SelectLayout select_layout(int depth_n, int width, int budget, int wmax) 
   L.off_npart = take(sizeof(int) * (depth_n + 2), 4);
   L.off_coff = take(sizeof(int) * 17, 4);
   L.off_wlen = take(sizeof(int) * (kSelectThreads / kWave) * wmax, 4);
+  L.off_cut = take(sizeof(int) * 3 * wmax, 4);
   L.off_info = take(sizeof(uint32_t) * std::max(1, L.tot), 4);
   L.off_order = take(sizeof(uint32_t) * std::max(1, budget), 4);
+  L.off_gida = take(sizeof(uint32_t) * std::max(1, budget), 4);
+  L.off_gidb = take(sizeof(uint32_t) * std::max(1, budget), 4);
   L.off_gidx = take(sizeof(uint16_t) * std::max(1, L.tot), 2);
   L.bytes = (o + 15) / 16 * 16;
   return L;
@@ -131,18 +135,8 @@ __device__ __forceinline__ double uniform(double v) {
 // Number of binary-search steps over n entries: ceil(log2(n + 1)).
 __device__ __forceinline__ int bitwidth(int n) { return n > 0 ? 32 - __clz(n) : 0; }
 
-// Same-level order of two candidates (score, info = parent position | rank << 16).
-__device__ __forceinline__ bool precedes_level(double sa, uint32_t ia, double sb, uint32_t ib) {
-  if (sa != sb) return sa > sb;
-  const uint32_t pa = ia & 0xFFFFu, pb = ib & 0xFFFFu;
-  if (pa != pb) return pa < pb;
-  return (ia >> 16) < (ib >> 16);
-}
-
-// Wave argmax of (value, id) under `better`, through DPP lane moves into lane
-// 63, then broadcast: quad swaps, rotations by 4 and 8 inside each row of 16
-// lanes, row broadcasts 15 and 31 (the order is total, so any combination
-// order gives the same winner).  Lanes a move does not reach keep their pair.
+// One step of a lane argmax: take the (value, id) pair a DPP lane move brings
+// when it is better.  Lanes the move does not reach (row mask) keep their pair.
 template <int CTRL, int ROW_MASK>
 __device__ __forceinline__ void dpp_better(float& v, int& id) {
   const float ov = __builtin_bit_cast(
@@ -152,59 +146,85 @@ __device__ __forceinline__ void dpp_better(float& v, int& id) {
   if (better(ov, oi, v, id)) { v = ov; id = oi; }
 }
 
-__device__ __forceinline__ void wave_best_all(float& v, int& id) {
+// Segmented argmax of (value, id) under `better` over SEG = 16, 32 or 64
+// lanes, through DPP lane moves: quad swaps and rotations by 4 and 8 leave
+// every lane of a row of 16 with the row's best; row broadcasts 15 (and 31)
+// carry it into the next row (and the upper half), and the segment's last
+// lane is read back (the order is total, so any combination order gives the
+// same winner).
+template <int SEG>
+__device__ __forceinline__ void seg_best_all(float& v, int& id) {
   dpp_better<0xB1, 0xF>(v, id);   // quad_perm [1, 0, 3, 2]
   dpp_better<0x4E, 0xF>(v, id);   // quad_perm [2, 3, 0, 1]
   dpp_better<0x124, 0xF>(v, id);  // row_ror 4
   dpp_better<0x128, 0xF>(v, id);  // row_ror 8
-  dpp_better<0x142, 0xA>(v, id);  // row_bcast 15 into rows 1 and 3
-  dpp_better<0x143, 0xC>(v, id);  // row_bcast 31 into rows 2 and 3
-  v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), kWave - 1));
-  id = __builtin_amdgcn_readlane(id, kWave - 1);
+  if constexpr (SEG >= 32) {
+    dpp_better<0x142, 0xA>(v, id);  // row_bcast 15 into rows 1 and 3
+    if constexpr (SEG == 64) {
+      dpp_better<0x143, 0xC>(v, id);  // row_bcast 31 into rows 2 and 3
+      v = __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+      id = __builtin_amdgcn_readlane(id, 63);
+    } else {
+      const bool hi = (threadIdx.x % kWave) >= 32;
+      const int v31 = __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 31);
+      const int v63 = __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63);
+      const int i31 = __builtin_amdgcn_readlane(id, 31);
+      const int i63 = __builtin_amdgcn_readlane(id, 63);
+      v = __builtin_bit_cast(float, hi ? v63 : v31);
+      id = hi ? i63 : i31;
+    }
+  }
 }
 
-// Merge the chunk partials of every depth of sequence seq (one wave a depth;
-// each lane holds one chunk's sorted candidates in registers): lse[d], the
-// top-W (cval, ctok [d * WMAX + r]) and, when part_ent is given, the entropy
+// Merge the chunk partials of every depth of sequence seq: one segment of SEG
+// lanes a depth (SEG >= chunks; each lane holds one chunk's sorted candidates
+// in registers), 64 / SEG depths a wave.  Writes lse[d], the top-W
+// (cval, ctok [d * WMAX + r]) and, when part_ent is given, the entropy
 // ent[d] = log S - T / S with S = sum exp(x - max), T = sum exp(x - max)(x - max).
-template <int WMAX>
-__device__ void merge_depth_partials(const float* __restrict__ part_max,
-                                     const double* __restrict__ part_sum,
-                                     const double* __restrict__ part_ent,
-                                     const float* __restrict__ part_val,
-                                     const int* __restrict__ part_idx, int chunks, int depth_n,
-                                     int width, int seq, double* lse, double* ent, float* cval,
-                                     int* ctok, int32_t* err, int nwaves) {
+// Lanes past `chunks` add zeros, so the sums equal those of a 64-lane
+// butterfly whatever SEG is.
+template <int WMAX, int SEG>
+__device__ __forceinline__ void merge_depth_partials_seg(const float* __restrict__ part_max,
+                                         const double* __restrict__ part_sum,
+                                         const double* __restrict__ part_ent,
+                                         const float* __restrict__ part_val,
+                                         const int* __restrict__ part_idx, int chunks, int depth_n,
+                                         int width, int seq, double* lse, double* ent,
+                                         float* cval, int* ctok, int32_t* err, int nwaves) {
+  constexpr int PER_WAVE = kWave / SEG;
   const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
-  for (int d = wv; d < depth_n; d += nwaves) {
-    const size_t row = static_cast<size_t>(seq) * depth_n + d;
-    const bool act = lane < chunks;
-    const float mc = act ? part_max[row * chunks + lane] : -INFINITY;
-    const double sc = act ? part_sum[row * chunks + lane] : 0.0;
+  const int sl = lane % SEG, sg = lane / SEG;
+  for (int d0 = wv * PER_WAVE; d0 < depth_n; d0 += nwaves * PER_WAVE) {
+    const int d = d0 + sg;
+    const bool dok = d < depth_n;
+    const size_t row = static_cast<size_t>(seq) * depth_n + (dok ? d : 0);
+    const bool act = dok && sl < chunks;
+    const float mc = act ? part_max[row * chunks + sl] : -INFINITY;
+    const double sc = act ? part_sum[row * chunks + sl] : 0.0;
     float hv[WMAX];
     int hid[WMAX];
 #pragma unroll
     for (int k = 0; k < WMAX; ++k) {
       const bool ok = act && k < width;
-      hv[k] = ok ? part_val[(row * chunks + lane) * width + k] : -INFINITY;
-      hid[k] = ok ? part_idx[(row * chunks + lane) * width + k] : INT32_MAX;
+      hv[k] = ok ? part_val[(row * chunks + sl) * width + k] : -INFINITY;
+      hid[k] = ok ? part_idx[(row * chunks + sl) * width + k] : INT32_MAX;
     }
     float M = mc;
-    for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, shfl_xor(M, o));
+    for (int o = SEG / 2; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o, SEG));
     const double scale =
         (mc == -INFINITY) ? 0.0 : exp(static_cast<double>(mc) - static_cast<double>(M));
     double contrib = sc * scale;
-    for (int o = 32; o > 0; o >>= 1) contrib += shfl_xor_f64(contrib, o);
+    for (int o = SEG / 2; o > 0; o >>= 1) contrib += __shfl_xor(contrib, o, SEG);
     double tsum = 0.0;
     if (part_ent) {
       // the chunk's terms were taken about its own max mc: shift them to M
-      const double tc = act ? part_ent[row * chunks + lane] : 0.0;
+      const double tc = act ? part_ent[row * chunks + sl] : 0.0;
       tsum = (mc == -INFINITY)
                  ? 0.0
                  : scale * (tc + (static_cast<double>(mc) - static_cast<double>(M)) * sc);
-      for (int o = 32; o > 0; o >>= 1) tsum += shfl_xor_f64(tsum, o);
+      for (int o = SEG / 2; o > 0; o >>= 1) tsum += __shfl_xor(tsum, o, SEG);
     }
-    if (lane == 0) {
+    if (sl == 0 && dok) {
       if (M == -INFINITY) {
         report(err, JT_DERR_BAD_LOGIT);
         lse[d] = 0.0;
@@ -217,16 +237,48 @@ __device__ void merge_depth_partials(const float* __restrict__ part_max,
     for (int r = 0; r < width; ++r) {
       float bv = hv[0];
       int bi = hid[0];
-      wave_best_all(bv, bi);
+      seg_best_all<SEG>(bv, bi);
       if (hid[0] == bi && bi != INT32_MAX) {  // this lane's head won: pop it
 #pragma unroll
         for (int k = 0; k + 1 < WMAX; ++k) { hv[k] = hv[k + 1]; hid[k] = hid[k + 1]; }
         hv[WMAX - 1] = -INFINITY;
         hid[WMAX - 1] = INT32_MAX;
       }
-      if (lane == 0) { cval[d * WMAX + r] = bv; ctok[d * WMAX + r] = bi; }
+      if (sl == 0 && dok) { cval[d * WMAX + r] = bv; ctok[d * WMAX + r] = bi; }
     }
   }
+}
+
+template <int WMAX>
+__device__ __forceinline__ void merge_depth_partials(const float* __restrict__ part_max,
+                                     const double* __restrict__ part_sum,
+                                     const double* __restrict__ part_ent,
+                                     const float* __restrict__ part_val,
+                                     const int* __restrict__ part_idx, int chunks, int depth_n,
+                                     int width, int seq, double* lse, double* ent, float* cval,
+                                     int* ctok, int32_t* err, int nwaves) {
+  if (chunks <= 16)
+    merge_depth_partials_seg<WMAX, 16>(part_max, part_sum, part_ent, part_val, part_idx, chunks,
+                                       depth_n, width, seq, lse, ent, cval, ctok, err, nwaves);
+  else if (chunks <= 32)
+    merge_depth_partials_seg<WMAX, 32>(part_max, part_sum, part_ent, part_val, part_idx, chunks,
+                                       depth_n, width, seq, lse, ent, cval, ctok, err, nwaves);
+  else
+    merge_depth_partials_seg<WMAX, 64>(part_max, part_sum, part_ent, part_val, part_idx, chunks,
+                                       depth_n, width, seq, lse, ent, cval, ctok, err, nwaves);
+}
+
+// Sum over aligned groups of N = 1, 2, 4, 8 or 16 lanes, left in every lane
+// of the group, through DPP moves: quad_perm swaps within quads, then the
+// half-row and row mirrors (lane i meets lane 7 - i, then 15 - i: after the
+// quad sums, those pairs hold the two halves' sums).
+template <int N>
+__device__ __forceinline__ int group_sum(int v) {
+  if constexpr (N >= 2) v += __builtin_amdgcn_update_dpp(0, v, 0xB1, 0xF, 0xF, false);   // [1,0,3,2]
+  if constexpr (N >= 4) v += __builtin_amdgcn_update_dpp(0, v, 0x4E, 0xF, 0xF, false);   // [2,3,0,1]
+  if constexpr (N >= 8) v += __builtin_amdgcn_update_dpp(0, v, 0x141, 0xF, 0xF, false);  // half mirror
+  if constexpr (N >= 16) v += __builtin_amdgcn_update_dpp(0, v, 0x140, 0xF, 0xF, false); // mirror
+  return v;
 }
 
 struct RankArgs {
@@ -240,8 +292,10 @@ struct RankArgs {
   const int* wlen;        // this wave's copy of the column lengths
   const float* cv;        // this level's draft values (top-W log-probs before normalising)
   const float* cvn;       // the next level's
+  int* cut_next;          // per column of the next level: first entry below tau (atomic min)
   int width, cap, cap_n;  // cap_n: the next level's capacity (0: no next level)
   double s_next;          // S of the next level
+  double tau;
   int threads;
 };
 
@@ -266,36 +320,37 @@ __device__ __forceinline__ void rank_entries(const RankArgs& a, const int (&lens
       int cnt = 0;
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
-        int lo[KC], hi[KC], base[KC], pt[KC];
+        // pos[j]: the preceding prefix of column k2 found so far; steps of
+        // 2^(csteps-1), ..., 1 cover any length below 2^csteps (>= m_prev)
+        int pos[KC], len[KC], pt[KC];
+        const double* col[KC];
 #pragma unroll
         for (int j = 0; j < KC; ++j) {
           const int k2 = sub + (g * KC + j) * LPC;
-          lo[j] = 0;
-          hi[j] = k2 != k ? a.wlen[k2] : 0;
-          base[j] = a.coff[k2];
-          pt[j] = p + (k2 < k ? 1 : 0);  // on equal scores, (q, k2) precedes iff q < pt
+          pos[j] = 0;
+          len[j] = k2 != k ? a.wlen[k2] : 0;
+          col[j] = a.cand + a.coff[k2] - 1;  // col[q] = entry q - 1
+          pt[j] = p + (k2 < k ? 1 : 0);  // on equal scores, entry q - 1 precedes iff q <= pt
         }
-        for (int step = 0; step < csteps; ++step) {
+        for (int half = (1 << csteps) >> 1; half > 0; half >>= 1) {
           double v[KC];
-          // mid <= hi <= the column's capacity: at worst the first slot past
-          // the column, still inside the buffers, and then unused
+          // entry min(pos + half, len) - 1: inside the column, or for an empty
+          // column the slot before it (still inside LDS, and then unused)
 #pragma unroll
-          for (int j = 0; j < KC; ++j) v[j] = a.cand[base[j] + ((lo[j] + hi[j]) >> 1)];
+          for (int j = 0; j < KC; ++j) v[j] = col[j][min(pos[j] + half, len[j])];
 #pragma unroll
           for (int j = 0; j < KC; ++j) {
-            const int mid = (lo[j] + hi[j]) >> 1;
-            const int pr = static_cast<int>(v[j] > sc) |
-                           (static_cast<int>(v[j] == sc) & static_cast<int>(mid < pt[j]));
-            const int act = static_cast<int>(lo[j] < hi[j]);
-            lo[j] = (act & pr) ? mid + 1 : lo[j];
-            hi[j] = (act & (pr ^ 1)) ? mid : hi[j];
+            const int q = pos[j] + half;
+            const int pr = static_cast<int>(q <= len[j]) &
+                           (static_cast<int>(v[j] > sc) |
+                            (static_cast<int>(v[j] == sc) & static_cast<int>(q <= pt[j])));
+            pos[j] = pr ? q : pos[j];
           }
         }
 #pragma unroll
-        for (int j = 0; j < KC; ++j) cnt += lo[j];
+        for (int j = 0; j < KC; ++j) cnt += pos[j];
       }
-#pragma unroll
-      for (int o = 1; o < LPC; o <<= 1) cnt += shfl_xor(cnt, o);
+      cnt = group_sum<LPC>(cnt);
       const int rank = p + cnt;
       if (rank < a.cap) {
         const double raw = a.raw_prev[p] + static_cast<double>(a.cv[k]);
@@ -308,8 +363,11 @@ __device__ __forceinline__ void rank_entries(const RankArgs& a, const int (&lens
 #pragma unroll
         for (int j = 0; j < KC * NG; ++j) {
           const int k2 = sub + j * LPC;
-          if (k2 < a.width && (rank + 1) * (k2 + 1) <= a.cap_n)  // rank < cap_n / (k2 + 1)
-            a.cand_next[a.coff[k2] + rank] = (raw + static_cast<double>(a.cvn[k2])) - a.s_next;
+          if (k2 < a.width && (rank + 1) * (k2 + 1) <= a.cap_n) {  // rank < cap_n / (k2 + 1)
+            const double cs = (raw + static_cast<double>(a.cvn[k2])) - a.s_next;
+            a.cand_next[a.coff[k2] + rank] = cs;
+            if (cs < a.tau) atomicMin(&a.cut_next[k2], rank);
+          }
         }
       }
     }
@@ -341,6 +399,8 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   double* lv_score = reinterpret_cast<double*>(smem + L.off_score);
   double* g_a = reinterpret_cast<double*>(smem + L.off_ga);
   double* g_b = reinterpret_cast<double*>(smem + L.off_gb);
+  uint32_t* gid_a = reinterpret_cast<uint32_t*>(smem + L.off_gida);
+  uint32_t* gid_b = reinterpret_cast<uint32_t*>(smem + L.off_gidb);
   float* cval = reinterpret_cast<float*>(smem + L.off_cval);
   int* ctok = reinterpret_cast<int*>(smem + L.off_ctok);
   int* loff = reinterpret_cast<int*>(smem + L.off_loff);
@@ -348,6 +408,7 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   int* npart = reinterpret_cast<int*>(smem + L.off_npart);
   int* coff = reinterpret_cast<int*>(smem + L.off_coff);  // column offsets (LDS copy)
   int* wlen_all = reinterpret_cast<int*>(smem + L.off_wlen);
+  int* cutb = reinterpret_cast<int*>(smem + L.off_cut);  // [3][WMAX], rotating by level
   uint32_t* lv_info = reinterpret_cast<uint32_t*>(smem + L.off_info);
   uint32_t* order = reinterpret_cast<uint32_t*>(smem + L.off_order);  // node - 1 -> level << 16 | pos
   uint16_t* lv_gidx = reinterpret_cast<uint16_t*>(smem + L.off_gidx);
@@ -410,24 +471,36 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   const int t1 = max(64, 2 * ((budget + depth_n - 1) / depth_n));
   double tau = -INFINITY;
   int last_level = 0;
+  double* g_old = g_a;  // G: scores, with each entry's (level << 16 | position)
+  double* g_new = g_b;
+  uint32_t* gi_old = gid_a;
+  uint32_t* gi_new = gid_b;
+  int gn = 0;
+  bool g_complete = false;  // pass 1 held the whole selection
   for (int pass = 1; pass <= 2; ++pass) {
     const bool merge_g = pass == 1;
     const int tmax = pass == 1 ? t1 : budget;
-    const int rank_threads = merge_g ? kSelectThreads - kWave : kSelectThreads;
+    // pass 1 leaves at least one wave to the G merge
+    const int max_rank_threads = merge_g ? kSelectThreads - kWave : kSelectThreads;
     double* raw_prev = raw_a;
     double* raw_cur = raw_b;
     double* cand_cur = cand_a;
     double* cand_nxt = cand_b;
-    double* g_old = g_a;
-    double* g_new = g_b;
-    // level 1's columns: the children of the root (raw 0)
-    if (tid < width && tid < WMAX) {
+    // level 1's columns: the children of the root (raw 0), and their cut
+    if (tid < 3 * WMAX) {
+      const int k = tid % WMAX;
       const int c1 = min(loff[2] - loff[1], tmax);
-      if (tid < c1) cand_a[coff[tid]] = (0.0 + static_cast<double>(cval[tid])) - S[1];
+      int cut = INT_MAX;
+      if (k < width && k < c1) {
+        const double cs = (0.0 + static_cast<double>(cval[k])) - S[1];
+        if (tid < WMAX) cand_a[coff[k]] = cs;
+        if (tid / WMAX == 1 && cs < tau) cut = 0;
+      }
+      cutb[tid] = cut;
     }
     if (tid == 0) raw_a[0] = 0.0;
     __syncthreads();
-    int m_prev = 1, gn = 0;
+    int m_prev = 1;
     bool complete = true;  // pass 1: no truncated level ends at or above tau1 (checked below)
     last_level = 0;
     for (int d = 1;; ++d) {
@@ -436,19 +509,16 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
       const int cap = min(cap_full, tmax);
       const bool grow = cap > 0 && m_prev > 0;
       // column lengths, cut at tau: lane k of every wave searches column k
+      // column lengths: lane k of every wave holds column k's, cut where the
+      // writers of the column found it drop below tau
+      int* cut_cur = cutb + (d % 3) * WMAX;
+      int* cut_nxt = cutb + ((d + 1) % 3) * WMAX;
+      const double tau_w = tau;
       int myl = 0;
-      if (grow && lane < width && lane < WMAX) {
-        int hi = min(m_prev, cap / (lane + 1));
-        if (tau != -INFINITY) {
-          const double* col = cand_cur + coff[lane];
-          int lo = 0;
-          while (lo < hi) {
-            const int mid = (lo + hi) >> 1;
-            if (col[mid] >= tau) lo = mid + 1; else hi = mid;
-          }
-        }
-        myl = hi;
-      }
+      if (grow && lane < width && lane < WMAX)
+        myl = min(min(m_prev, cap / (lane + 1)), cut_cur[lane]);
+      // the buffer the next round writes was last read in the previous round
+      if (tid < WMAX) cutb[((d + 2) % 3) * WMAX + tid] = INT_MAX;
       // every wave keeps its own LDS copy of the column lengths (read by lane)
       if (lane < WMAX) wlen_all[(tid / kWave) * WMAX + lane] = myl;
       int lens[WMAX];
@@ -463,15 +533,18 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
       const double Sn = cap_n > 0 ? uniform(S[d + 1]) : 0.0;
       // lanes per entry: as many as keep every entry within one round
       int lpc = WMAX;
-      while (lpc > 1 && total_a * lpc > rank_threads) lpc >>= 1;
+      while (lpc > 1 && total_a * lpc > max_rank_threads) lpc >>= 1;
       const int cpl = WMAX / lpc;  // columns per lane
       const int items = total_a * lpc;
+      // the waves the ranking leaves free merge G
+      const int rank_threads =
+          merge_g ? min(max_rank_threads, (items + kWave - 1) / kWave * kWave) : kSelectThreads;
       const int csteps = bitwidth(m_prev);
       if (tid < rank_threads) {
         const RankArgs ra{cand_cur, cand_nxt, raw_prev, raw_cur, lv_score + loff[d],
                           lv_info + loff[d], coff, wlen_all + (tid / kWave) * WMAX,
                           cval + (d - 1) * WMAX, cap_n > 0 ? cval + d * WMAX : cval,
-                          width, cap, cap_n, Sn, rank_threads};
+                          cut_nxt, width, cap, cap_n, Sn, tau_w, rank_threads};
         switch (cpl) {
           case 1: rank_entries<WMAX, 1, 1>(ra, lens, items, csteps); break;
           case 2: rank_entries<WMAX, 2, 1>(ra, lens, items, csteps); break;
@@ -480,13 +553,14 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
           default: rank_entries<WMAX, 4, 4>(ra, lens, items, csteps); break;
         }
       } else if (merge_g && d >= 2) {
-        // the last wave merges level d-1 into G (stable: G first on equal
-        // scores), each lane a run of consecutive outputs found by merge path
+        // the remaining threads merge level d-1 into G (stable: G first on
+        // equal scores), each a run of consecutive outputs found by merge path
         const int mb = m_prev;
         const double* lvl = lv_score + loff[d - 1];
         const int n_out = min(budget, gn + mb);
-        const int per = (n_out + kWave - 1) / kWave;
-        const int o0 = min(lane * per, n_out), o1 = min(o0 + per, n_out);
+        const int gthreads = kSelectThreads - rank_threads;
+        const int per = (n_out + gthreads - 1) / gthreads;
+        const int o0 = min((tid - rank_threads) * per, n_out), o1 = min(o0 + per, n_out);
         if (o0 < o1) {
           // i = number of G entries among the first o0 outputs
           int lo = max(0, o0 - mb), hi = min(o0, gn);
@@ -498,6 +572,8 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
           for (int o = o0; o < o1; ++o) {
             const bool take_g = i < gn && (j >= mb || g_old[i] >= lvl[j]);
             g_new[o] = take_g ? g_old[i] : lvl[j];
+            gi_new[o] = take_g ? gi_old[i]
+                               : (static_cast<uint32_t>(d - 1) << 16) | static_cast<uint32_t>(j);
             i += take_g ? 1 : 0;
             j += take_g ? 0 : 1;
           }
@@ -507,6 +583,7 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
       if (merge_g && d >= 2 && m_prev > 0) {
         gn = min(budget, gn + m_prev);
         double* g = g_old; g_old = g_new; g_new = g;
+        uint32_t* gi = gi_old; gi_old = gi_new; gi_new = gi;
         if (gn >= budget && budget > 0) tau = uniform(g_old[budget - 1]);
       }
       if (!grow) break;
@@ -517,7 +594,11 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
       m_prev = m_d;
       last_level = d;
     }
-    if (pass == 2 || complete) break;
+    if (pass == 2) break;
+    if (complete) {
+      g_complete = true;
+      break;
+    }
     // a full truncated level is fine when its last entry scores below tau1
     complete = true;
     for (int d0 = 1; d0 <= last_level; d0 += kWave) {
@@ -529,7 +610,10 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
       }
       if (__ballot(bad) != 0) complete = false;
     }
-    if (complete) break;
+    if (complete) {
+      g_complete = true;
+      break;
+    }
     __syncthreads();  // pass 2 overwrites the levels every thread has just read
   }
   if (tid == 0)
@@ -562,6 +646,22 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   }
   tot_part = uniform(tot_part);
   maxpart = uniform(maxpart);
+  // When pass 1 held the selection, G is its top B in score order; with no
+  // equal scores among them and no other entry at tau, that is the global
+  // order itself.
+  bool from_g = g_complete && gn >= budget && budget > 0 && tot_part == budget;
+  if (from_g) {
+    const bool tie = tid + 1 < budget && g_old[tid] == g_old[tid + 1];
+    from_g = __syncthreads_or(tie) == 0;
+  }
+  if (from_g) {
+    for (int o = tid; o < budget; o += kSelectThreads) {
+      const uint32_t id = gi_old[o];
+      order[o] = id;
+      lv_gidx[loff[id >> 16] + (id & 0xFFFFu)] = static_cast<uint16_t>(o + 1);
+    }
+    tot_part = 0;  // nothing left to rank
+  }
   int lpc = 16, lpc_log = 4;
   while (lpc > 1 && (tot_part * lpc > kSelectThreads || lpc / 2 >= last_level)) {
     lpc >>= 1;
@@ -611,7 +711,7 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
       lv_gidx[loff[d] + i] = static_cast<uint16_t>(rank + 1);
     }
   }
-  const int n_sel = min(budget, tot_part);
+  const int n_sel = from_g ? budget : min(budget, tot_part);
   __syncthreads();
 
   // ---- phase 4: write the tree in node-index order
