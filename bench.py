@@ -10,7 +10,10 @@ acceptance over [257, 151936] fp32 target logits per sequence.
 
 Printed: one JSON line.  ``value`` is tree-node tokens per second of the whole
 step (sum of n_nodes over the batch / step time); the attention kernel is
-additionally reported as KV GB/s and against the bf16 MFMA roofline.
+additionally reported as KV GB/s and against the bf16 MFMA roofline.  The
+same run also times the step on the pages' other settings (budget 16 and 256
+at batch 1, batch 16/32 serving; ``configs``) and two probes of this box's
+practical ceilings (a device copy and a large bf16 GEMM; ``probes``).
 """
 from __future__ import annotations
 
@@ -25,6 +28,8 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 WORKLOAD = "qwen3_30b_a3b_b8"
+# the other settings timed in the same run (shorter: they are secondary lines)
+SECONDARY = ("tiny_f32", "qwen3_8b_b16", "qwen3_8b_b256", "serving_b16", "serving_b32")
 PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
 
@@ -38,6 +43,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seqs", type=int, default=8,
                     help="sequences of the workload the CPU oracle is timed on")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="time only the main workload, not the secondary settings")
+    ap.add_argument("--config-steps", type=int, default=20)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only copy BYTES device-to-device --steps times (a plain copy of known "
                          "size, the reference that HBM byte counters are scaled by)")
@@ -112,6 +120,50 @@ def algorithmic_work(w, prefix, n_nodes, depth):
     return kv, q, fl
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def probes():
+    """Practical ceilings measured on this machine: a 1 GiB device copy (read +
+    write bytes) and an 8192^3 bf16 GEMM through the vendor library."""
+    import torch
+    out = {}
+    a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda:0")
+    b = torch.empty_like(a)
+    a.fill_(1)
+    for _ in range(3):
+        b.copy_(a)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(10):
+        b.copy_(a)
+    e1.record()
+    torch.cuda.synchronize()
+    out["copy_gbps"] = 2 * (1 << 30) * 10 / e0.elapsed_time(e1) / 1e6
+    del a, b
+    n = 8192
+    x = torch.randn((n, n), dtype=torch.bfloat16, device="cuda:0")
+    y = torch.randn((n, n), dtype=torch.bfloat16, device="cuda:0")
+    for _ in range(3):
+        torch.matmul(x, y)
+    e0.record()
+    for _ in range(10):
+        torch.matmul(x, y)
+    e1.record()
+    torch.cuda.synchronize()
+    out["gemm_bf16_tflops"] = 2 * n ** 3 * 10 / e0.elapsed_time(e1) / 1e9
+    return out
+
+
 def cpu_baseline(w, x, seqs):
     """The CPU oracle, untouched, on the first ``seqs`` sequences of the batch."""
     import numpy as np
@@ -136,9 +188,143 @@ def cpu_baseline(w, x, seqs):
         nodes += n
     dt = time.perf_counter() - t0
     return {"value": nodes / dt, "unit": "tree-node tok/s", "cores": int(threads),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "kind": "oracle",
             "sample": f"{seqs} of {w.batch} sequences of the same workload, whole verify step "
                       f"(build, mask, attention, accept) in fp64 NumPy; {dt:.2f} s"}
+
+
+class Verify:
+    """One workload's inputs in HBM, its outputs and workspaces (allocated
+    once, outside any timed region) and the verify step on the current stream."""
+
+    def __init__(self, B, w, dev):
+        import torch
+        self.B, self.w = B, w
+        x = self.x = make_inputs_for(w)
+        self.d_draft = x.draft.to(dev)
+        self.d_target = x.target.to(dev)
+        self.d_q, self.d_k, self.d_v = x.q.to(dev), x.k_pool.to(dev), x.v_pool.to(dev)
+        self.d_prefix, self.d_table = x.prefix_len.to(dev), x.page_table.to(dev)
+        self.d_root = x.root_token.to(dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        b, T = w.batch, w.max_nodes
+        lib = B.load()
+        self.ws_build = torch.empty(max(1, lib.jt_build_tree_workspace(
+            b, w.depth_n, w.vocab, w.width_w, w.budget_b)), dtype=torch.uint8, device=dev)
+        self.ws_attn = torch.empty(max(1, lib.jt_tree_attention_workspace(
+            b, T, w.hq, w.hkv, w.head_dim, x.page_table.shape[1], 16,
+            B.JT_BF16 if w.dtype == "bf16" else B.JT_F32)), dtype=torch.uint8, device=dev)
+        self.ws_acc = torch.empty(max(1, lib.jt_accept_workspace(b, T, w.vocab)),
+                                  dtype=torch.uint8, device=dev)
+        self.anc = torch.empty((b, T, (T + 31) // 32), dtype=torch.int32, device=dev)
+        self.out = torch.empty_like(self.d_q)
+        self.lse = torch.empty((b, T, w.hq), dtype=torch.float32, device=dev)
+        self.stream = torch.cuda.current_stream()
+        self.ev = {k: [] for k in ("s0", "s1", "s2", "s3", "s4")}
+
+    def step(self, record):
+        import torch
+        B, w, ev, st = self.B, self.w, self.ev, self.stream
+
+        def mark(k):
+            if record:
+                e = torch.cuda.Event(enable_timing=True)
+                e.record(st)
+                ev[k].append(e)
+        mark("s0")
+        tree = B.jt_build_tree(self.d_draft, w.width_w, w.budget_b, self.d_root, err=self.err,
+                               workspace=self.ws_build)
+        mark("s1")
+        B.jt_tree_meta(tree["parent"], tree["n_nodes"], err=self.err, out=self.anc)
+        mark("s2")
+        B.jt_tree_attention(self.d_q, self.d_k, self.d_v, tree["n_nodes"], self.d_prefix,
+                            self.d_table, self.x.num_pages, self.anc, w.scale, err=self.err,
+                            out=self.out, lse=self.lse, workspace=self.ws_attn)
+        mark("s3")
+        res = B.jt_accept(self.d_target, w.depth_n, tree["parent"], tree["token"],
+                          tree["depth"], tree["n_nodes"], err=self.err, workspace=self.ws_acc)
+        mark("s4")
+        return tree, res
+
+    def run(self, steps, warmup):
+        """Warm up, then time `steps` steps: wall clock around them (synchronised
+        on both sides) and HIP events between the stages."""
+        import torch
+        for _ in range(warmup):
+            self.step(False)
+        torch.cuda.synchronize()
+        for k_ in self.ev:
+            self.ev[k_].clear()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            tree, res = self.step(True)
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t0
+        if int(self.err.item()) != 0:
+            raise RuntimeError(f"{self.w.name}: device error bits {int(self.err.item())}")
+        return wall * 1000.0 / steps, tree, res
+
+    def avg(self, a, b_):
+        ev = self.ev
+        return sum(x_.elapsed_time(y_) for x_, y_ in zip(ev[a], ev[b_])) / len(ev[a])
+
+    def pct(self, a, b_):
+        import numpy as np
+        ev = self.ev
+        v = np.sort([x_.elapsed_time(y_) for x_, y_ in zip(ev[a], ev[b_])])
+        return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
+                "p90": float(np.percentile(v, 90))}
+
+    def stage_ms(self):
+        return {"build_tree": self.avg("s0", "s1"), "tree_meta": self.avg("s1", "s2"),
+                "tree_attention": self.avg("s2", "s3"), "accept": self.avg("s3", "s4")}
+
+    def attention_figures(self, tree, t_attn_ms):
+        w = self.w
+        n_nodes = tree["n_nodes"].cpu().numpy()
+        depth = tree["depth"].cpu().numpy()
+        kv_bytes, qo_bytes, flops = algorithmic_work(w, self.x.prefix_len.numpy(), n_nodes,
+                                                     depth)
+        t = t_attn_ms / 1000.0
+        return {"tokens": int(n_nodes.sum()), "kv_bytes": kv_bytes, "qo_bytes": qo_bytes,
+                "flops": flops, "tflops": flops / t / 1e12, "kv_gbps": kv_bytes / t / 1e9}
+
+
+def make_inputs_for(w):
+    from tree_causal_attention_amd import workloads as WL
+    return WL.make_inputs(w)
+
+
+def secondary_line(B, name, dev, steps, warmup, peaks):
+    """Step time, stage times and the attention's rates for one more setting."""
+    import torch
+    from tree_causal_attention_amd import workloads as WL
+    w = WL.WORKLOADS[name]
+    v = Verify(B, w, dev)
+    ms_step, tree, res = v.run(steps, warmup)
+    st = v.stage_ms()
+    fig = v.attention_figures(tree, st["tree_attention"])
+    line = {
+        "workload": f"batch {w.batch}, prefix {w.prefix}, {w.hq}q/{w.hkv}kv heads, head_dim "
+                    f"{w.head_dim}, {w.dtype}, B={w.budget_b}, W={w.width_w}, N={w.depth_n}, "
+                    f"vocab {w.vocab}",
+        "ms_per_step": ms_step,
+        "tree_nodes_per_step": fig["tokens"],
+        "tok_per_s": fig["tokens"] / (ms_step / 1000.0),
+        "stage_ms": st,
+        "attention": {
+            "tflops": fig["tflops"],
+            "frac_mfma_peak": fig["tflops"] / PEAK_BF16_TFLOPS,
+            "frac_gemm_probe": fig["tflops"] / peaks["gemm_bf16_tflops"],
+            "kv_gbps": fig["kv_gbps"],
+            "frac_hbm_peak": fig["kv_gbps"] / PEAK_HBM_GBPS,
+            "frac_copy_probe": fig["kv_gbps"] / peaks["copy_gbps"],
+        },
+        "accept_len": res[0].cpu().tolist()[:8],
+    }
+    del v
+    torch.cuda.empty_cache()
+    return line
 
 
 def main():
@@ -149,97 +335,32 @@ def main():
     if args.copy_probe > 0:
         copy_probe(args.copy_probe, args.steps)
         return
-    import numpy as np
     import torch
     from tree_causal_attention_amd import binding as B
     from tree_causal_attention_amd import workloads as WL
 
     w = WL.WORKLOADS[args.workload]
     dev = torch.device("cuda:0")
-    x = WL.make_inputs(w)
-    d_draft = x.draft.to(dev)
-    d_target = x.target.to(dev)
-    d_q, d_k, d_v = x.q.to(dev), x.k_pool.to(dev), x.v_pool.to(dev)
-    d_prefix, d_table, d_root = x.prefix_len.to(dev), x.page_table.to(dev), x.root_token.to(dev)
-    err = torch.zeros(1, dtype=torch.int32, device=dev)
-    b, T = w.batch, w.max_nodes
-
-    # outputs and workspaces allocated once, outside the timed region
-    lib = B.load()
-    ws_build = torch.empty(max(1, lib.jt_build_tree_workspace(b, w.depth_n, w.vocab, w.width_w,
-                                                              w.budget_b)), dtype=torch.uint8,
-                           device=dev)
-    ws_attn = torch.empty(max(1, lib.jt_tree_attention_workspace(
-        b, T, w.hq, w.hkv, w.head_dim, x.page_table.shape[1], 16, B.JT_BF16 if w.dtype == "bf16"
-        else B.JT_F32)), dtype=torch.uint8, device=dev)
-    ws_acc = torch.empty(max(1, lib.jt_accept_workspace(b, T, w.vocab)), dtype=torch.uint8,
-                         device=dev)
-    anc = torch.empty((b, T, (T + 31) // 32), dtype=torch.int32, device=dev)
-    out = torch.empty_like(d_q)
-    lse = torch.empty((b, T, w.hq), dtype=torch.float32, device=dev)
-    stream = torch.cuda.current_stream()
-    ev = {k: [] for k in ("s0", "s1", "s2", "s3", "s4")}
-
-    def step(record):
-        if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s0"].append(e)
-        tree = B.jt_build_tree(d_draft, w.width_w, w.budget_b, d_root, err=err, workspace=ws_build)
-        if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s1"].append(e)
-        B.jt_tree_meta(tree["parent"], tree["n_nodes"], err=err, out=anc)
-        if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s2"].append(e)
-        B.jt_tree_attention(d_q, d_k, d_v, tree["n_nodes"], d_prefix, d_table, x.num_pages, anc,
-                            w.scale, err=err, out=out, lse=lse, workspace=ws_attn)
-        if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s3"].append(e)
-        res = B.jt_accept(d_target, w.depth_n, tree["parent"], tree["token"], tree["depth"],
-                          tree["n_nodes"], err=err, workspace=ws_acc)
-        if record:
-            e = torch.cuda.Event(enable_timing=True); e.record(stream); ev["s4"].append(e)
-        return tree, res
-
-    for _ in range(args.warmup):
-        step(False)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    for _ in range(args.steps):
-        tree, res = step(True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    if int(err.item()) != 0:
-        raise RuntimeError(f"device error bits {int(err.item())}")
-
-    def avg(a, b_):
-        return sum(x_.elapsed_time(y_) for x_, y_ in zip(ev[a], ev[b_])) / len(ev[a])
-
-    def pct(a, b_):
-        v = np.sort([x_.elapsed_time(y_) for x_, y_ in zip(ev[a], ev[b_])])
-        return {"p10": float(np.percentile(v, 10)), "p50": float(np.percentile(v, 50)),
-                "p90": float(np.percentile(v, 90))}
-    stage_ms = {"build_tree": avg("s0", "s1"), "tree_meta": avg("s1", "s2"),
-                "tree_attention": avg("s2", "s3"), "accept": avg("s3", "s4")}
-    stage_pct = {"step": pct("s0", "s4"), "tree_attention": pct("s2", "s3")}
+    v = Verify(B, w, dev)
+    ms_step, tree, res = v.run(args.steps, args.warmup)
+    stage_ms = v.stage_ms()
+    stage_pct = {"step": v.pct("s0", "s4"), "tree_attention": v.pct("s2", "s3")}
 
     # the same step with the 256 MB last-level cache and L2 flushed before each
     # step (an untimed 1 GiB write), timed step by step with events
     flush = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-    for k_ in ev:
-        ev[k_].clear()
+    for k_ in v.ev:
+        v.ev[k_].clear()
     for _ in range(args.steps):
         flush.fill_(1)
-        step(True)
+        v.step(True)
     torch.cuda.synchronize()
-    flushed = {"step": pct("s0", "s4"), "tree_attention": pct("s2", "s3")}
+    flushed = {"step": v.pct("s0", "s4"), "tree_attention": v.pct("s2", "s3")}
     del flush
-    ms_step = wall * 1000.0 / args.steps
-    n_nodes = tree["n_nodes"].cpu().numpy()
-    depth = tree["depth"].cpu().numpy()
-    kv_bytes, qo_bytes, flops = algorithmic_work(w, x.prefix_len.numpy(), n_nodes, depth)
-    t_attn = stage_ms["tree_attention"] / 1000.0
-    achieved_tflops = flops / t_attn / 1e12
-    kv_gbps = kv_bytes / t_attn / 1e9
-    tokens = int(n_nodes.sum())
+    fig = v.attention_figures(tree, stage_ms["tree_attention"])
+    peaks = probes()
+    achieved_tflops = fig["tflops"]
+    tokens = fig["tokens"]
     result = {
         "metric": "tree-attn verify tree-node tok/s + KV GB/s at B=256; % of HBM/MFMA peak",
         "value": tokens / (ms_step / 1000.0),
@@ -268,20 +389,30 @@ def main():
             "unit": "TFLOP/s",
             "frac": achieved_tflops / PEAK_BF16_TFLOPS,
             "traffic": measured_traffic(w.name),
-            "algorithmic_flops": flops,
-            "algorithmic_bytes": kv_bytes + qo_bytes,
+            "algorithmic_flops": fig["flops"],
+            "algorithmic_bytes": fig["kv_bytes"] + fig["qo_bytes"],
+            "frac_gemm_probe": achieved_tflops / peaks["gemm_bf16_tflops"],
         },
-        "kv_gbps": kv_gbps,
-        "kv_hbm_frac": kv_gbps / PEAK_HBM_GBPS,
+        "kv_gbps": fig["kv_gbps"],
+        "kv_hbm_frac": fig["kv_gbps"] / PEAK_HBM_GBPS,
+        "kv_copy_probe_frac": fig["kv_gbps"] / peaks["copy_gbps"],
+        "probes": peaks,
         "stage_ms": stage_ms,
         "stage_ms_pct": stage_pct,
         "flushed_ms_pct": flushed,
         "accept_len": res[0].cpu().tolist(),
     }
-    result["next_rows"] = time_next_rows(B, w, x, tree, d_draft, d_target, d_k, d_v, d_prefix,
-                                         d_table, d_root, ws_build, ws_acc, err, stream)
+    result["next_rows"] = time_next_rows(B, w, v.x, tree, v.d_draft, v.d_target, v.d_k, v.d_v,
+                                         v.d_prefix, v.d_table, v.d_root, v.ws_build, v.ws_acc,
+                                         v.err, v.stream)
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(w, x, min(args.cpu_seqs, w.batch))
+        result["cpu_baseline"] = cpu_baseline(w, v.x, min(args.cpu_seqs, w.batch))
+    if not args.no_configs:
+        del v
+        torch.cuda.empty_cache()
+        result["configs"] = {
+            name: secondary_line(B, name, dev, args.config_steps, max(3, args.warmup // 2), peaks)
+            for name in SECONDARY if name != w.name}
     print(json.dumps(result))
 
 

@@ -36,6 +36,26 @@ __device__ __forceinline__ void load_vec(const T* x, int i, float (&v)[VEC]) {
 
 constexpr int kCandCap = 1024;  // threshold candidates kept per chunk
 
+// e^y in fp64 for finite y <= 0, table-driven (Tang's method): y = k c + r
+// with c = ln2 / 256, |r| <= c / 2, so e^y = 2^(k >> 8) * 2^((k & 255) / 256)
+// * e^r; the table holds 2^(j / 256) and e^r is its degree-5 Taylor
+// polynomial (truncation below 2^-64 relative).  c is split into a 32-bit
+// head (k * c_hi is exact for |k| < 2^21, i.e. y > -5600) and a tail.
+__device__ __forceinline__ double exp_nonpos(double y, const double* __restrict__ exp2_tbl) {
+  constexpr double kInvC = 369.3299304675746;       // 256 / ln2
+  constexpr double kCHi = 0.00270760617331689;      // ln2 / 256, leading 32 bits
+  constexpr double kCLo = 7.453964567463233e-13;    // ln2 / 256 - kCHi
+  const double kd = rint(y * kInvC);
+  const double r = fma(-kd, kCLo, fma(-kd, kCHi, y));
+  const int k = static_cast<int>(kd);
+  double p = fma(r, 1.0 / 120.0, 1.0 / 24.0);
+  p = fma(p, r, 1.0 / 6.0);
+  p = fma(p, r, 0.5);
+  p = fma(p, r, 1.0);
+  p = fma(p, r, 1.0);
+  return ldexp(exp2_tbl[k & 255] * p, k >> 8);
+}
+
 // One workgroup per (vocab chunk, depth row); thread t holds EPT logits of
 // the chunk in registers (16-byte loads, one pass over HBM).
 //  * max and the fp64 sum of exp(x - max) come straight from the registers;
@@ -63,8 +83,11 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   __shared__ float sm_L;
   __shared__ float sm_v[kScanThreads / kWave];
   __shared__ int sm_i[kScanThreads / kWave];
+  __shared__ double sm_exp2[256];  // 2^(j / 256)
+  static_assert(kScanThreads >= 256, "one table entry a thread");
 
   const int row = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
+  if (t < 256) sm_exp2[t] = exp2(static_cast<double>(t) * (1.0 / 256.0));
   const int lane = t % kWave, wv = t / kWave;
   const int begin = c * chunk_len;
   const int end = min(vocab, begin + chunk_len);
@@ -123,8 +146,10 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
     const double Md = static_cast<double>(M);
 #pragma unroll
     for (int k = 0; k < EPT; ++k) {
-      const double dx = static_cast<double>(fmaxf(xv[k], -1.0e30f)) - Md;
-      const double e = exp(dx);
+      // x >= -1e30: dx is finite, and e^dx underflows to 0 well before the
+      // table method's range ends; -inf entries are dropped below
+      const double dx = fmax(static_cast<double>(fmaxf(xv[k], -1.0e30f)) - Md, -5000.0);
+      const double e = exp_nonpos(dx, sm_exp2);
       const bool fin = xv[k] != -INFINITY;
       sacc += fin ? e : 0.0;
       if constexpr (ENT) tacc += fin ? e * dx : 0.0;

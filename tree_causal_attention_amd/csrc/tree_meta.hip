@@ -15,7 +15,7 @@
 
 namespace jt {
 
-constexpr int kMetaThreads = 256;
+constexpr int kMetaThreads = 1024;
 constexpr int kMaxNodes = 1024;
 
 __global__ __launch_bounds__(kMetaThreads) void tree_meta_kernel(
