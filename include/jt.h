@@ -49,24 +49,42 @@
 extern "C" {
 #endif
 
+/* Every enum below also lists its type's full int32 range (the _RANGE_
+ * members are never valid arguments): any int a caller passes is then a
+ * value of the type, which the library rejects with JT_ERR_INVALID_ARG,
+ * rather than an out-of-range enum value that C++ leaves undefined. */
 typedef enum {
+  JT_STATUS_RANGE_MIN_ = INT32_MIN,
   JT_OK = 0,
   JT_ERR_INVALID_ARG = 1,  /* a null pointer, a negative or inconsistent size */
   JT_ERR_UNSUPPORTED = 2,  /* valid but outside what the kernels implement    */
   JT_ERR_WORKSPACE = 3,    /* workspace NULL or smaller than the query says    */
   JT_ERR_LAUNCH = 4,       /* a HIP kernel launch failed                       */
-  JT_ERR_SCRATCH = 5       /* inputs exceed jt_accept_noalloc's static scratch */
+  JT_ERR_SCRATCH = 5,      /* inputs exceed jt_accept_noalloc's static scratch */
+  JT_STATUS_RANGE_MAX_ = INT32_MAX
 } jt_status;
 
-typedef enum { JT_F32 = 0, JT_BF16 = 1 } jt_dtype;
+typedef enum {
+  JT_DTYPE_RANGE_MIN_ = INT32_MIN,
+  JT_F32 = 0,
+  JT_BF16 = 1,
+  JT_DTYPE_RANGE_MAX_ = INT32_MAX
+} jt_dtype;
 
 /* Tree expansion of jt_build_tree_variant. */
-typedef enum { JT_EXPAND_CANDIDATE = 0, JT_EXPAND_NODE_BLOCK = 1 } jt_expand;
+typedef enum {
+  JT_EXPAND_RANGE_MIN_ = INT32_MIN,
+  JT_EXPAND_CANDIDATE = 0,
+  JT_EXPAND_NODE_BLOCK = 1,
+  JT_EXPAND_RANGE_MAX_ = INT32_MAX
+} jt_expand;
 
 /* How the drafted tokens of a tree were proposed (jt_accept_stochastic). */
 typedef enum {
+  JT_DRAFT_RANGE_MIN_ = INT32_MIN,
   JT_DRAFT_TOPW = 0,    /* siblings are distinct chosen tokens (jt_build_tree's top-W) */
-  JT_DRAFT_SAMPLED = 1  /* every child drawn i.i.d. from softmax(draft row / T)        */
+  JT_DRAFT_SAMPLED = 1, /* every child drawn i.i.d. from softmax(draft row / T)        */
+  JT_DRAFT_RANGE_MAX_ = INT32_MAX
 } jt_draft_mode;
 
 /* Device error bits (OR-ed into *err). */

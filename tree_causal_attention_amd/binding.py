@@ -15,7 +15,9 @@ import os
 import torch
 
 HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(HERE, "libjt.so")
+# JT_LIBRARY selects another build of the same library (e.g. the host-only
+# sanitized one that the CPU checks of the C ABI's validation load)
+LIB_PATH = os.environ.get("JT_LIBRARY") or os.path.join(HERE, "libjt.so")
 
 JT_F32, JT_BF16 = 0, 1
 JT_EXPAND_CANDIDATE, JT_EXPAND_NODE_BLOCK = 0, 1

@@ -30,6 +30,7 @@ const char* jt_status_string(jt_status s) {
     case JT_ERR_WORKSPACE: return "workspace missing or too small";
     case JT_ERR_LAUNCH: return "kernel launch failed";
     case JT_ERR_SCRATCH: return "inputs need more than the no-allocation entry point's scratch";
+    default: break;
   }
   return "unknown status";
 }
