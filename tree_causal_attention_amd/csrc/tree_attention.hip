@@ -106,7 +106,7 @@ struct AttnArgs {
   const uint32_t* anc;
   uint16_t* out;
   float* lse;
-  float* part_o;    // partial rows [ngroups * part_rows_group, D]
+  _Float16* part_o;  // partial rows [ngroups * part_rows_group, D], normalised, fp16
   float* part_lse;  // [ngroups * part_rows_group]
   int32_t* err;
   int max_nodes, hq, hkv, group, max_pages, num_pages, nwords;
@@ -556,15 +556,22 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   } else {
     const size_t prow = static_cast<size_t>(item.sg) * a.part_rows_group +
                         part_row(a, item.rt, item.sp) + (r - rowbase);
-    float* op = a.part_o + prow * D;
+    // a normalised partial row lies within the range of the values (|o| <=
+    // max |v|): fp16 keeps it to 2^-11 relative, four times finer than the
+    // bf16 output, at half the bytes of fp32 to write here and read back
+    _Float16* op = a.part_o + prow * D;
 #pragma unroll
     for (int db = 0; db < DB; ++db)
 #pragma unroll
       for (int grp = 0; grp < 4; ++grp) {
         const int d0 = db * 32 + 8 * grp + 4 * h;
-        *reinterpret_cast<float4*>(op + d0) =
-            make_float4(o_acc[db][4 * grp] * inv, o_acc[db][4 * grp + 1] * inv,
-                        o_acc[db][4 * grp + 2] * inv, o_acc[db][4 * grp + 3] * inv);
+        typedef __attribute__((ext_vector_type(4))) _Float16 h4;
+        h4 hv;
+        hv.x = static_cast<_Float16>(o_acc[db][4 * grp] * inv);
+        hv.y = static_cast<_Float16>(o_acc[db][4 * grp + 1] * inv);
+        hv.z = static_cast<_Float16>(o_acc[db][4 * grp + 2] * inv);
+        hv.w = static_cast<_Float16>(o_acc[db][4 * grp + 3] * inv);
+        *reinterpret_cast<h4*>(op + d0) = hv;
       }
     if (h == 0) a.part_lse[prow] = lse_v;
   }
@@ -616,8 +623,8 @@ __global__ __launch_bounds__(256) void tree_attn_combine(AttnArgs a) {
     }
     wsum += wl;
     const int cnt = min(kWave, splits - c0);
-    const float* po = a.part_o + (gbase + sp0 + static_cast<size_t>(c0) * kRowsWG) * D +
-                      lane * PER;
+    const _Float16* po = a.part_o + (gbase + sp0 + static_cast<size_t>(c0) * kRowsWG) * D +
+                         lane * PER;
     // kUnroll splits per round, all loads issued before the first use; slots
     // past cnt reload the last split and get weight 0 (their lanes hold 0)
     for (int k0 = 0; k0 < cnt; k0 += kUnroll) {
@@ -626,7 +633,8 @@ __global__ __launch_bounds__(256) void tree_attn_combine(AttnArgs a) {
       for (int kk = 0; kk < kUnroll; ++kk) {
         const int kc = min(k0 + kk, cnt - 1);
 #pragma unroll
-        for (int e = 0; e < PER; ++e) v[kk][e] = po[static_cast<size_t>(kc) * kRowsWG * D + e];
+        for (int e = 0; e < PER; ++e)
+          v[kk][e] = static_cast<float>(po[static_cast<size_t>(kc) * kRowsWG * D + e]);
       }
 #pragma unroll
       for (int kk = 0; kk < kUnroll; ++kk) {
@@ -777,7 +785,7 @@ static AttnPlan attn_plan(const AttnShape& s) {
   }
   if (p.part_rows_group > 0) {
     const size_t rows = static_cast<size_t>(p.ngroups) * p.part_rows_group;
-    p.off_lse = (rows * s.head_dim * sizeof(float) + 255) / 256 * 256;
+    p.off_lse = (rows * s.head_dim * sizeof(_Float16) + 255) / 256 * 256;
     p.bytes = p.off_lse + (rows * sizeof(float) + 255) / 256 * 256;
   }
   return p;
@@ -828,7 +836,7 @@ hipError_t tree_attention_launch(const AttnShape& sh, const void* q, const void*
   a.anc = anc_mask;
   a.out = static_cast<uint16_t*>(out);
   a.lse = lse;
-  a.part_o = p.part_rows_group > 0 ? static_cast<float*>(workspace) : nullptr;
+  a.part_o = p.part_rows_group > 0 ? static_cast<_Float16*>(workspace) : nullptr;
   a.part_lse = p.part_rows_group > 0
                    ? reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + p.off_lse)
                    : nullptr;
