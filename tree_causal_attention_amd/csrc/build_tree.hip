@@ -418,24 +418,43 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
   const int lane = tid % kWave;
   const int nwaves = kSelectThreads / kWave;
 
+  // set-up that needs nothing from phase 1
+  if (tid <= depth_n + 1) loff[tid] = L.loff[tid];
+  if (tid <= WMAX) coff[tid] = L.coff[tid];
+  if (tid == 0) lcnt[0] = 1;
+  for (int x = tid; x < L.tot; x += kSelectThreads) lv_gidx[x] = 0xFFFF;
+
+  // Level 1's columns (the children of the root, raw 0) and their cut at tau.
+  // Reads S_1 = 0 + lse_0 and the offsets from the arguments, so pass 1 can
+  // set them up in the same step as S.
+  auto init_level1 = [&](int tmax, double tau0) {
+    if (tid < 3 * WMAX) {
+      const int k = tid % WMAX;
+      const int c1 = min(L.loff[2] - L.loff[1], tmax);
+      int cut = INT_MAX;
+      if (k < width && k < c1) {
+        const double cs = (0.0 + static_cast<double>(cval[k])) - (0.0 + lse[0]);
+        if (tid < WMAX) cand_a[L.coff[k]] = cs;
+        if (tid / WMAX == 1 && cs < tau0) cut = 0;
+      }
+      cutb[tid] = cut;
+    }
+    if (tid == 0) raw_a[0] = 0.0;
+  };
+
   // ---- phase 1: merge the chunk partials of every depth
   merge_depth_partials<WMAX>(part_max, part_sum, nullptr, part_val, part_idx, chunks, depth_n,
                              width, seq, lse, nullptr, cval, ctok, err, nwaves);
   __syncthreads();
-  if (tid <= depth_n + 1) {
+  if (tid <= depth_n) {
     // S_d = lse_0 + ... + lse_{d-1}, summed in that order
     double sd = 0.0;
     for (int j = 0; j < depth_n; ++j) {
       const double v = lse[j];
       if (j < tid) sd += v;
     }
-    if (tid <= depth_n) S[tid] = sd;
-    loff[tid] = L.loff[tid];
+    S[tid] = sd;
   }
-  if (tid <= WMAX) coff[tid] = L.coff[tid];
-  if (tid == 0) lcnt[0] = 1;
-  for (int x = tid; x < L.tot; x += kSelectThreads) lv_gidx[x] = 0xFFFF;
-  __syncthreads();
 
   // ---- phase 2: level by level, the best children in key order.
   // The candidates of level d form W columns: column k holds the children
@@ -486,20 +505,8 @@ __global__ __launch_bounds__(kSelectThreads) void tree_select(
     double* raw_cur = raw_b;
     double* cand_cur = cand_a;
     double* cand_nxt = cand_b;
-    // level 1's columns: the children of the root (raw 0), and their cut
-    if (tid < 3 * WMAX) {
-      const int k = tid % WMAX;
-      const int c1 = min(loff[2] - loff[1], tmax);
-      int cut = INT_MAX;
-      if (k < width && k < c1) {
-        const double cs = (0.0 + static_cast<double>(cval[k])) - S[1];
-        if (tid < WMAX) cand_a[coff[k]] = cs;
-        if (tid / WMAX == 1 && cs < tau) cut = 0;
-      }
-      cutb[tid] = cut;
-    }
-    if (tid == 0) raw_a[0] = 0.0;
-    __syncthreads();
+    init_level1(tmax, tau);
+    __syncthreads();  // pass 1: also S and the set-up above
     int m_prev = 1;
     bool complete = true;  // pass 1: no truncated level ends at or above tau1 (checked below)
     last_level = 0;
