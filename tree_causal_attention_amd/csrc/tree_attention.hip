@@ -763,7 +763,13 @@ static AttnPlan attn_plan(const AttnShape& s) {
   // splits for the same finishing time.
   if (full_items > 0 && full_items < 192 && p.has_partial) {
     const int gx = (p.ngroups + kXcds - 1) / kXcds;
-    const int sf1 = static_cast<int>(kCusPerXcd / (gx * (p.rt_full + kPartialTileCost)));
+    // the most full-tile splits whose items, with the partial tile's, still
+    // fit the XCD's CUs once
+    int sf1 = 0;
+    for (int sf = 1; sf <= max_splits; ++sf) {
+      const int sp = std::max(1, static_cast<int>(kPartialTileCost * sf + 0.5));
+      if (gx * (p.rt_full * sf + sp) <= static_cast<int>(kCusPerXcd)) sf1 = sf;
+    }
     if (sf1 >= 2) {
       const int sp1 = std::max(1, static_cast<int>(kPartialTileCost * sf1 + 0.5));
       p.s_full = std::max(min_splits, std::min(sf1, max_splits));
