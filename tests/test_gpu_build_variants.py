@@ -144,3 +144,26 @@ def test_variant_max_budget(expand):
             if t["margin"] < _GAP or t["cross_ties"]:
                 continue
             _check_seq(g, s, t)
+
+
+@pytest.mark.parametrize("expand", ["candidate", "node_block"])
+def test_variant_cross_depth_entropy_ties(expand):
+    """Pure entropy priority (a = 1) with draft rows repeated at several
+    depths: a repeated row has the same entropy at every depth it sits at, on
+    both sides (same data, same arithmetic), so entries of different depths
+    tie exactly and the tie rule alone decides.  The trees must agree bit for
+    bit, and the oracle must report such ties (the case is exercised)."""
+    rng = np.random.default_rng(77 if expand == "candidate" else 78)
+    N, W, V, Bn = 6, 3, 40, 60
+    base = rng.standard_normal((3, V)) * 2
+    rows = base[[0, 0, 1, 1, 2, 0]]  # depths 1, 2 and 6 share a row; 3 and 4 too
+    L = torch.from_numpy(np.stack([rows, rows[::-1].copy()]).astype(np.float32))
+    roots = [3, 7]
+    g, err = _gpu_variant(L, W, Bn, roots, expand, 1.0)
+    assert err == 0
+    ties = 0
+    for s in range(2):
+        t = O.build_tree_variant(L[s].numpy(), W, Bn, roots[s], expand, 1.0)
+        ties += t["cross_ties"]
+        _check_seq(g, s, t)
+    assert ties > 0
