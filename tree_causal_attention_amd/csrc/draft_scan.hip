@@ -149,7 +149,9 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
       // x >= -1e30: dx is finite, and e^dx underflows to 0 well before the
       // table method's range ends; -inf entries are dropped below
       const double dx = fmax(static_cast<double>(fmaxf(xv[k], -1.0e30f)) - Md, -5000.0);
-      const double e = exp_nonpos(dx, sm_exp2);
+      double e;
+      if constexpr (EPT <= 32) e = exp_nonpos(dx, sm_exp2);
+      else e = exp(dx);  // long chunks (vocab > 2^19): the table code unrolled 128x compiles slowly
       const bool fin = xv[k] != -INFINITY;
       sacc += fin ? e : 0.0;
       if constexpr (ENT) tacc += fin ? e * dx : 0.0;
