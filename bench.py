@@ -247,19 +247,26 @@ class Verify:
         return tree, res
 
     def run(self, steps, warmup):
-        """Warm up, then time `steps` steps: wall clock around them (synchronised
-        on both sides) and HIP events between the stages."""
+        """Warm up, then two passes of `steps` steps.  The timed pass has the
+        wall clock around it (synchronised on both sides) and nothing but the
+        steps inside; it gives the step time.  The breakdown pass right after
+        records HIP events between the stages; each event costs the stream a
+        few microseconds (≈ 3 µs on MI355X), so its stages add up to a little
+        more than the timed step."""
         import torch
         for _ in range(warmup):
             self.step(False)
         torch.cuda.synchronize()
-        for k_ in self.ev:
-            self.ev[k_].clear()
         t0 = time.perf_counter()
         for _ in range(steps):
-            tree, res = self.step(True)
+            tree, res = self.step(False)
         torch.cuda.synchronize()
         wall = time.perf_counter() - t0
+        for k_ in self.ev:
+            self.ev[k_].clear()
+        for _ in range(steps):
+            self.step(True)
+        torch.cuda.synchronize()
         if int(self.err.item()) != 0:
             raise RuntimeError(f"{self.w.name}: device error bits {int(self.err.item())}")
         return wall * 1000.0 / steps, tree, res

@@ -131,6 +131,33 @@ __global__ __launch_bounds__(kWalkThreads) void accept_walk(
   __shared__ int bad;
   __shared__ unsigned int best_key;
   const int seq = blockIdx.x, v = threadIdx.x;
+  const size_t base = static_cast<size_t>(seq) * max_nodes;
+  // Every slot's inputs are loaded while the node count is still in flight
+  // (each array spans max_nodes per sequence; slots past the count hold stale
+  // values that are never used).  The chunk winners are loaded kBatch at a
+  // time, all loads before the first comparison.
+  constexpr int kBatch = 8;
+  float bv = -INFINITY;
+  int bi = INT32_MAX, pv = -1, dv = 0, tv = 0;
+  if (v < max_nodes) {
+    pv = parent[base + v];
+    dv = depth[base + v];
+    tv = token[base + v];
+    const size_t o = (base + v) * chunks;
+    for (int c0 = 0; c0 < chunks; c0 += kBatch) {
+      float cv[kBatch];
+      int ci[kBatch];
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k) {
+        const int c = min(c0 + k, chunks - 1);  // repeats of the last chunk change nothing
+        cv[k] = part_val[o + c];
+        ci[k] = part_idx[o + c];
+      }
+#pragma unroll
+      for (int k = 0; k < kBatch; ++k)
+        if (better(cv[k], ci[k], bv, bi)) { bv = cv[k]; bi = ci[k]; }
+    }
+  }
   const int n = n_nodes[seq];
   int32_t* nodes_out = accept_nodes + static_cast<size_t>(seq) * depth_n;
   if (n < 1 || n > max_nodes) {
@@ -144,17 +171,11 @@ __global__ __launch_bounds__(kWalkThreads) void accept_walk(
   }
   if (v == 0) { bad = 0; best_key = 0u; }
   __syncthreads();
-  const size_t base = static_cast<size_t>(seq) * max_nodes;
   if (v < n) {
-    const size_t o = (base + v) * chunks;
-    float bv = part_val[o];
-    int bi = part_idx[o];
-    for (int c = 1; c < chunks; ++c)
-      if (better(part_val[o + c], part_idx[o + c], bv, bi)) { bv = part_val[o + c]; bi = part_idx[o + c]; }
     a[v] = bi;
     mx[v] = bv;
-    par[v] = parent[base + v];
-    dep[v] = depth[base + v];
+    par[v] = pv;
+    dep[v] = dv;
     acc[v] = (v == 0) ? 1 : 0;
   }
   __syncthreads();
@@ -166,7 +187,7 @@ __global__ __launch_bounds__(kWalkThreads) void accept_walk(
       const int p = par[v];
       if (p < 0 || p >= v) b = JT_DERR_BAD_PARENT;
       else if (dep[v] != dep[p] + 1 || dep[v] > depth_n) b = JT_DERR_BAD_DEPTH;
-      else if (mode == 1 && (token[base + v] < 0 || token[base + v] >= vocab)) b = JT_DERR_BAD_TOKEN;
+      else if (mode == 1 && (tv < 0 || tv >= vocab)) b = JT_DERR_BAD_TOKEN;
     }
     if (b) atomicOr(&bad, b);
   }
@@ -184,7 +205,7 @@ __global__ __launch_bounds__(kWalkThreads) void accept_walk(
   bool pass = false;
   if (v < n && v > 0) {
     const int p = par[v];
-    const int t = token[base + v];
+    const int t = tv;
     if (mode == 0) {
       pass = t == a[p];
     } else {

@@ -58,6 +58,7 @@ constexpr int kMaxTilesItem = kMaxPagesLds * kPage / kKT;
 // fewest key tiles per split of a row tile: shorter splits cost more in
 // per-workgroup set-up and partial rows than they gain in parallelism
 constexpr int kMinTilesSplit = 4;
+constexpr int kCombineWaves = 4;      // waves per merge workgroup
 constexpr int kXcds = 8;             // MI355X: 8 XCDs, workgroups dealt round-robin
 constexpr double kCusPerXcd = 32.0;  // 256 CUs
 constexpr double kPartialTileCost = 0.625;  // partial-tile / full-tile time per key tile
@@ -577,22 +578,32 @@ __global__ __launch_bounds__(kAttnThreads) void tree_attn_mfma(AttnArgs a) {
   }
 }
 
-// Merges the per-split partials of the row tiles that were split: one wave
-// per row.  The split log-sum-exps are spread over the lanes (max and weight
-// sum by shuffles), then each lane accumulates its D / 64 output columns over
-// the splits with the loads of several splits in flight.
+// Merges the per-split partials of the row tiles that were split.  A row is
+// served by D / 8 lanes, each owning 8 output columns (one 16-byte load of
+// fp16 per split), so a wave merges 64 / (D / 8) rows.  The lanes of a row
+// spread its split log-sum-exps between them (max and weight sum by shuffles
+// inside the row's lanes), then accumulate their columns over the splits with
+// the loads of several splits in flight.
 template <int D>
-__global__ __launch_bounds__(256) void tree_attn_combine(AttnArgs a) {
-  constexpr int PER = D / kWave;  // output columns per lane
+constexpr int combine_rows_per_block() { return kCombineWaves * kWave / (D / 8); }
+
+template <int D>
+__global__ __launch_bounds__(kCombineWaves * kWave) void tree_attn_combine(AttnArgs a) {
+  constexpr int LPR = D / 8;                         // lanes per row
+  constexpr int RPB = combine_rows_per_block<D>();   // rows per block
   constexpr int kUnroll = 8;
-  // blocks of 4 rows: kRowsWG / 4 per split full row tile, then enough for
+  static_assert(LPR % kUnroll == 0 && kWave % LPR == 0, "row lanes must tile the wave");
+  typedef __attribute__((ext_vector_type(8))) _Float16 h8;
+  // blocks of RPB rows: kRowsWG / RPB per split full row tile, then enough for
   // the rows of the split last row tile
+  constexpr int kBlocksTile = kRowsWG / RPB;
   const int ctiles_full = a.s_full > 1 ? a.rt_full : 0;
-  const int bfull = ctiles_full * (kRowsWG / 4);
-  const int ctile = blockIdx.x < bfull ? blockIdx.x / (kRowsWG / 4) : ctiles_full;
-  const int rloc = (blockIdx.x < bfull ? blockIdx.x % (kRowsWG / 4) : blockIdx.x - bfull) * 4 +
-                   threadIdx.x / kWave;
+  const int bfull = ctiles_full * kBlocksTile;
   const int lane = threadIdx.x % kWave;
+  const int sl = lane % LPR, sbase = lane - sl;  // lane inside the row, first lane of the row
+  const int rib = (threadIdx.x / kWave) * (kWave / LPR) + lane / LPR;  // row inside the block
+  const int ctile = blockIdx.x < bfull ? blockIdx.x / kBlocksTile : ctiles_full;
+  const int rloc = (blockIdx.x < bfull ? blockIdx.x % kBlocksTile : blockIdx.x - bfull) * RPB + rib;
   const int sg = blockIdx.y, s = sg / a.hkv, g = sg % a.hkv;
   const int rt = ctile < ctiles_full ? ctile : a.rt_full;
   const int splits = rt < a.rt_full ? a.s_full : a.s_part;
@@ -600,59 +611,62 @@ __global__ __launch_bounds__(256) void tree_attn_combine(AttnArgs a) {
   const int P = a.prefix_len[s];
   if (!seq_ok(n, P, a.max_nodes, a.max_pages, a.err, false)) return;
   const int r = rt * kRowsWG + rloc;
+  // every lane of a row leaves together, so the shuffles below stay inside rows
   if (r >= n * a.group) return;
   const int node = r / a.group, hq = g * a.group + r % a.group;
   const size_t gbase = static_cast<size_t>(sg) * a.part_rows_group + rloc;
   // partial row of split sp: gbase + sp0 + sp * kRowsWG
   const int sp0 = part_row(a, rt, 0);
+  const float* pl = a.part_lse + gbase + sp0;
   float M = -INFINITY;
-  for (int sp = lane; sp < splits; sp += kWave)
-    M = fmaxf(M, a.part_lse[gbase + sp0 + static_cast<size_t>(sp) * kRowsWG]);
+  for (int sp = sl; sp < splits; sp += LPR) M = fmaxf(M, pl[static_cast<size_t>(sp) * kRowsWG]);
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
-  float acc[PER];
+  for (int m = LPR / 2; m >= 1; m >>= 1) M = fmaxf(M, shfl_xor(M, m));
+  float acc[8];
 #pragma unroll
-  for (int k = 0; k < PER; ++k) acc[k] = 0.0f;
+  for (int k = 0; k < 8; ++k) acc[k] = 0.0f;
   float wsum = 0.0f;
-  for (int c0 = 0; c0 < splits; c0 += kWave) {
+  for (int c0 = 0; c0 < splits; c0 += LPR) {
     // this lane's split weight (0 for splits that saw no key of the row)
     float wl = 0.0f;
-    if (c0 + lane < splits) {
-      const float ls = a.part_lse[gbase + sp0 + static_cast<size_t>(c0 + lane) * kRowsWG];
+    if (c0 + sl < splits) {
+      const float ls = pl[static_cast<size_t>(c0 + sl) * kRowsWG];
       wl = (ls == -INFINITY) ? 0.0f : expf(ls - M);
     }
     wsum += wl;
-    const int cnt = min(kWave, splits - c0);
-    const _Float16* po = a.part_o + (gbase + sp0 + static_cast<size_t>(c0) * kRowsWG) * D +
-                         lane * PER;
+    const int cnt = min(LPR, splits - c0);
+    const _Float16* po = a.part_o + (gbase + sp0 + static_cast<size_t>(c0) * kRowsWG) * D + sl * 8;
     // kUnroll splits per round, all loads issued before the first use; slots
     // past cnt reload the last split and get weight 0 (their lanes hold 0)
     for (int k0 = 0; k0 < cnt; k0 += kUnroll) {
-      float v[kUnroll][PER];
+      h8 v[kUnroll];
 #pragma unroll
       for (int kk = 0; kk < kUnroll; ++kk) {
         const int kc = min(k0 + kk, cnt - 1);
-#pragma unroll
-        for (int e = 0; e < PER; ++e)
-          v[kk][e] = static_cast<float>(po[static_cast<size_t>(kc) * kRowsWG * D + e]);
+        v[kk] = *reinterpret_cast<const h8*>(po + static_cast<size_t>(kc) * kRowsWG * D);
       }
 #pragma unroll
       for (int kk = 0; kk < kUnroll; ++kk) {
-        const float wk = __shfl(wl, k0 + kk, kWave);
+        const float wk = __shfl(wl, sbase + k0 + kk, kWave);
         // a zero weight contributes nothing, whatever the partial holds
 #pragma unroll
-        for (int e = 0; e < PER; ++e) acc[e] += (wk != 0.0f) ? wk * v[kk][e] : 0.0f;
+        for (int e = 0; e < 8; ++e)
+          acc[e] += (wk != 0.0f) ? wk * static_cast<float>(v[kk][e]) : 0.0f;
       }
     }
   }
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) wsum += shfl_xor(wsum, m);
+  for (int m = LPR / 2; m >= 1; m >>= 1) wsum += shfl_xor(wsum, m);
   const float inv = 1.0f / wsum;
-  uint16_t* op = a.out + ((static_cast<size_t>(s) * a.max_nodes + node) * a.hq + hq) * D;
+  uint32_t pk[4];
 #pragma unroll
-  for (int k = 0; k < PER; ++k)
-    op[lane * PER + k] = __builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[k] * inv));
-  if (a.lse && lane == 0)
+  for (int k = 0; k < 4; ++k)
+    pk[k] = static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[2 * k] * inv))) |
+            (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, static_cast<__bf16>(acc[2 * k + 1] * inv)))
+             << 16);
+  uint16_t* op = a.out + ((static_cast<size_t>(s) * a.max_nodes + node) * a.hq + hq) * D;
+  *reinterpret_cast<uint4*>(op + sl * 8) = make_uint4(pk[0], pk[1], pk[2], pk[3]);
+  if (a.lse && sl == 0)
     a.lse[(static_cast<size_t>(s) * a.max_nodes + node) * a.hq + hq] = M + logf(wsum);
 }
 
@@ -781,10 +795,11 @@ static AttnPlan attn_plan(const AttnShape& s) {
   p.slots_per_xcd = gx_max * items;
   p.full_part_rows = p.s_full > 1 ? p.rt_full * p.s_full * kRowsWG : 0;
   p.part_rows_group = p.full_part_rows + ((p.has_partial && p.s_part > 1) ? p.s_part * kRowsWG : 0);
-  // merge blocks (4 rows each): the split full row tiles, then the rows of a
+  // merge blocks (rb rows each): the split full row tiles, then the rows of a
   // split last row tile
-  p.cblocks = (p.s_full > 1 ? p.rt_full * (kRowsWG / 4) : 0) +
-              ((p.has_partial && p.s_part > 1) ? (rmax - p.rt_full * kRowsWG + 3) / 4 : 0);
+  const int rb = s.head_dim == 64 ? combine_rows_per_block<64>() : combine_rows_per_block<128>();
+  p.cblocks = (p.s_full > 1 ? p.rt_full * (kRowsWG / rb) : 0) +
+              ((p.has_partial && p.s_part > 1) ? (rmax - p.rt_full * kRowsWG + rb - 1) / rb : 0);
   if (s.dt == JT_F32) {
     p.part_rows_group = 0;
     p.cblocks = 0;
@@ -809,7 +824,7 @@ static hipError_t launch_mfma(const AttnShape& sh, const AttnPlan& p, AttnArgs& 
                      stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || p.cblocks == 0) return e;
-  hipLaunchKernelGGL(tree_attn_combine<D>, dim3(p.cblocks, p.ngroups), dim3(256),
+  hipLaunchKernelGGL(tree_attn_combine<D>, dim3(p.cblocks, p.ngroups), dim3(kCombineWaves * kWave),
                      0, stream, a);
   return hipGetLastError();
 }

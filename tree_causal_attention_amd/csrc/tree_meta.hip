@@ -21,11 +21,16 @@ constexpr int kMaxNodes = 1024;
 __global__ __launch_bounds__(kMetaThreads) void tree_meta_kernel(
     const int32_t* __restrict__ parent, const int32_t* __restrict__ n_nodes, int max_nodes,
     uint32_t* __restrict__ anc, int32_t* err) {
+  static_assert(kMetaThreads >= kMaxNodes, "one thread per node slot");
   __shared__ int par[kMaxNodes];
   __shared__ int bad;
   const int seq = blockIdx.x;
   const int nw = (max_nodes + 31) / 32;
   uint32_t* out = anc + static_cast<size_t>(seq) * max_nodes * nw;
+  // every slot's parent id is loaded while the node count is still in flight
+  // (the array spans max_nodes per sequence); slots past the count are unused
+  const int j = threadIdx.x;
+  const int pj = (j < max_nodes) ? parent[static_cast<size_t>(seq) * max_nodes + j] : -1;
   const int n = n_nodes[seq];
   if (threadIdx.x == 0) bad = 0;
   __syncthreads();
@@ -34,11 +39,9 @@ __global__ __launch_bounds__(kMetaThreads) void tree_meta_kernel(
     for (int x = threadIdx.x; x < max_nodes * nw; x += kMetaThreads) out[x] = 0u;
     return;
   }
-  const int32_t* pr = parent + static_cast<size_t>(seq) * max_nodes;
-  for (int j = threadIdx.x; j < n; j += kMetaThreads) {
-    const int p = pr[j];
-    par[j] = p;
-    const bool ok = (j == 0) ? (p == -1) : (p >= 0 && p < j);
+  if (j < n) {
+    par[j] = pj;
+    const bool ok = (j == 0) ? (pj == -1) : (pj >= 0 && pj < j);
     if (!ok) atomicOr(&bad, 1);
   }
   __syncthreads();
