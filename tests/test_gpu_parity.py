@@ -214,9 +214,8 @@ SMALL_ATTN = [
     (1, [100], [1024], 1024, 16, 1, 128, "bf16"),
     (2, [0, 37], [1024, 999], 1024, 16, 1, 64, "bf16"),
     (1, [10], [1024], 1024, 16, 1, 64, "f32"),
-    # a last row tile of at most 16 rows folded into the full-tile
-    # workgroups: 8 rows (and a sequence without any), D = 64, 16 rows of one
-    # node with 16 workgroups (most with no keys of it), group 2 with no prefix
+    # small last row tiles beside full ones: 8 rows (and a sequence without
+    # any), D = 64, 16 rows of one node, group 2 with no prefix
     (2, [100, 20], [257, 256], 257, 8, 1, 128, "bf16"),
     (1, [60], [257], 257, 4, 1, 64, "bf16"),
     (1, [30], [257], 257, 16, 1, 128, "bf16"),
