@@ -246,8 +246,11 @@ jt_status jt_tree_meta(const int32_t* parent, const int32_t* n_nodes, int batch,
  *   err       JT_DERR_BAD_NNODES, JT_DERR_BAD_PREFIX (sequence skipped),
  *             JT_DERR_BAD_PAGE (that page's keys read as zero).
  * Arithmetic: bf16 inputs use bf16 MFMA with fp32 accumulation, probabilities
- * rounded to bf16 for the PV product, output rounded to bf16.  f32 inputs are
- * computed in fp32 throughout.
+ * rounded to bf16 for the PV product, output rounded to bf16.  Rows whose keys
+ * are split over several workgroups are merged from normalised partial rows
+ * kept in the workspace in fp16 (relative rounding 2^-11, finer than the bf16
+ * output) with fp32 log-sum-exps.  f32 inputs are computed in fp32
+ * throughout.
  * Limits: head_dim in {64, 128}, page_size == 16, num_q_heads a multiple of
  * num_kv_heads with num_q_heads / num_kv_heads <= 16, 1 <= max_nodes <= 1024,
  * max_pages_per_seq >= 1, num_pages >= 1.
