@@ -14,7 +14,12 @@
 
 namespace jt {
 
-constexpr int kScanThreads = 256;
+constexpr int kScanThreads = 256;       // threads of a scan workgroup on large grids
+constexpr int kScanThreadsSmall = 512;  // ... and on grids of at most kSmallScanGrid
+// Chunks are 8K logits either way; grids this small (one or two sequences)
+// finish sooner with the chunk spread over twice the threads (16 logits a
+// thread), larger ones sooner with 256 threads of 32 logits.
+constexpr int kSmallScanGrid = 512;
 
 template <typename T, int VEC>
 __device__ __forceinline__ void load_vec(const T* x, int i, float (&v)[VEC]) {
@@ -66,25 +71,25 @@ __device__ __forceinline__ double exp_nonpos(double y, const double* __restrict_
 //    builds its exact sorted top-W and W rounds of "best head" merge them.
 // ENT: also the fp64 sum of exp(x - max) * (x - max) (the chunk's entropy
 // partial; tree_select_seq merges it into the per-depth entropy).
-template <typename T, int WMAX, int VEC, int EPT, bool ENT>
-__global__ __launch_bounds__(kScanThreads) void draft_row_scan(
+template <typename T, int WMAX, int VEC, int EPT, bool ENT, int NT>
+__global__ __launch_bounds__(NT) void draft_row_scan(
     const T* __restrict__ logits, int vocab, int chunks, int chunk_len, int width,
     float* __restrict__ part_max, double* __restrict__ part_sum, double* __restrict__ part_ent,
     float* __restrict__ part_val, int* __restrict__ part_idx, int32_t* err) {
   constexpr int NV = EPT / VEC;
-  __shared__ float sm_m[kScanThreads / kWave];
-  __shared__ double sm_s[kScanThreads / kWave];
-  __shared__ double sm_t[kScanThreads / kWave];
+  __shared__ float sm_m[NT / kWave];
+  __shared__ double sm_s[NT / kWave];
+  __shared__ double sm_t[NT / kWave];
   constexpr int PW = (WMAX + 3) / 4;  // threshold offers per wave
-  __shared__ float sm_off[(kScanThreads / kWave) * PW];
+  __shared__ float sm_off[(NT / kWave) * PW];
   __shared__ float sm_cv[kCandCap];
   __shared__ int sm_ci[kCandCap];
   __shared__ int sm_n;
   __shared__ float sm_L;
-  __shared__ float sm_v[kScanThreads / kWave];
-  __shared__ int sm_i[kScanThreads / kWave];
+  __shared__ float sm_v[NT / kWave];
+  __shared__ int sm_i[NT / kWave];
   __shared__ double sm_exp2[256];  // 2^(j / 256)
-  static_assert(kScanThreads >= 256, "one table entry a thread");
+  static_assert(NT >= 256, "one table entry a thread");
 
   const int row = blockIdx.y, c = blockIdx.x, t = threadIdx.x;
   if (t < 256) sm_exp2[t] = exp2(static_cast<double>(t) * (1.0 / 256.0));
@@ -98,7 +103,7 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   float m = -INFINITY;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int i = begin + (j * kScanThreads + t) * VEC;
+    const int i = begin + (j * NT + t) * VEC;
     float v[VEC];
     if (i < end) {
       load_vec<T, VEC>(x, i, v);
@@ -138,7 +143,7 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   }
   __syncthreads();
   float M = sm_m[0];
-  for (int w = 1; w < kScanThreads / kWave; ++w) M = fmaxf(M, sm_m[w]);
+  for (int w = 1; w < NT / kWave; ++w) M = fmaxf(M, sm_m[w]);
 
   // ---- fp64 sum of exp(x - M) over the registers
   double sacc = 0.0, tacc = 0.0;
@@ -165,10 +170,10 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   }
 
   // ---- threshold: the W-th largest of the 4 * PW offers (ties by position)
-  if (t < (kScanThreads / kWave) * PW) {
+  if (t < (NT / kWave) * PW) {
     const float v = sm_off[t];
     int rank = 0;
-    for (int u = 0; u < (kScanThreads / kWave) * PW; ++u) {
+    for (int u = 0; u < (NT / kWave) * PW; ++u) {
       const float ou = sm_off[u];
       rank += (ou > v || (ou == v && u < t)) ? 1 : 0;
     }
@@ -177,19 +182,19 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   __syncthreads();
   if (t == 0) {
     double S = 0.0;
-    for (int w = 0; w < kScanThreads / kWave; ++w) S += sm_s[w];
+    for (int w = 0; w < NT / kWave; ++w) S += sm_s[w];
     part_max[row * chunks + c] = M;
     part_sum[row * chunks + c] = S;
     if constexpr (ENT) {
       double Tt = 0.0;
-      for (int w = 0; w < kScanThreads / kWave; ++w) Tt += sm_t[w];
+      for (int w = 0; w < NT / kWave; ++w) Tt += sm_t[w];
       part_ent[row * chunks + c] = Tt;
     }
   }
   const float L = sm_L;
 #pragma unroll
   for (int j = 0; j < NV; ++j) {
-    const int i = begin + (j * kScanThreads + t) * VEC;
+    const int i = begin + (j * NT + t) * VEC;
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
       if (i + e < end && xv[j * VEC + e] >= L) {
@@ -202,14 +207,14 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   const int nc = sm_n;
   const size_t out0 = (static_cast<size_t>(row) * chunks + c) * width;
   if (nc <= kCandCap) {
-    for (int q = t; q < nc; q += kScanThreads) {
+    for (int q = t; q < nc; q += NT) {
       const float vq = sm_cv[q];
       const int iq = sm_ci[q];
       int r = 0;
       for (int u = 0; u < nc; ++u) r += better(sm_cv[u], sm_ci[u], vq, iq) ? 1 : 0;
       if (r < width) { part_val[out0 + r] = vq; part_idx[out0 + r] = iq; }
     }
-    for (int r = nc + t; r < width; r += kScanThreads) {
+    for (int r = nc + t; r < width; r += NT) {
       part_val[out0 + r] = -INFINITY;
       part_idx[out0 + r] = INT32_MAX;
     }
@@ -225,7 +230,7 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
   for (int j = 0; j < NV; ++j) {
 #pragma unroll
     for (int e = 0; e < VEC; ++e) {
-      const int i = begin + (j * kScanThreads + t) * VEC + e;
+      const int i = begin + (j * NT + t) * VEC + e;
       const float y = xv[j * VEC + e];
       if (i < end && better(y, i, tv[WMAX - 1], ti[WMAX - 1])) {
         // Sorted insert as a select network: slot k keeps its entry if it
@@ -258,7 +263,7 @@ __global__ __launch_bounds__(kScanThreads) void draft_row_scan(
     __syncthreads();
     float gv = sm_v[0];
     int gi = sm_i[0];
-    for (int w = 1; w < kScanThreads / kWave; ++w)
+    for (int w = 1; w < NT / kWave; ++w)
       if (better(sm_v[w], sm_i[w], gv, gi)) { gv = sm_v[w]; gi = sm_i[w]; }
     if (t == 0) { part_val[out0 + r] = gv; part_idx[out0 + r] = gi; }
     if (ti[0] == gi && gi != INT32_MAX) {
@@ -277,14 +282,19 @@ template <typename T, int WMAX, int VEC, bool ENT>
 static void launch_scan(const void* logits, int vocab, int width, const ScanArgs& a,
                         hipStream_t stream) {
   const dim3 grid(a.chunks, a.rows);
-  if (a.ept == 32)
-    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 32, ENT>), grid, dim3(kScanThreads), 0,
-                       stream, static_cast<const T*>(logits), vocab, a.chunks, a.chunk_len,
-                       width, a.pm, a.ps, a.pe, a.pv, a.pi, a.err);
+  static_assert(kScanThreadsSmall * 16 == kScanThreads * 32, "both shapes cover one chunk");
+  if (a.ept == 32 && static_cast<long long>(a.chunks) * a.rows <= kSmallScanGrid)
+    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 16, ENT, kScanThreadsSmall>), grid,
+                       dim3(kScanThreadsSmall), 0, stream, static_cast<const T*>(logits), vocab,
+                       a.chunks, a.chunk_len, width, a.pm, a.ps, a.pe, a.pv, a.pi, a.err);
+  else if (a.ept == 32)
+    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 32, ENT, kScanThreads>), grid,
+                       dim3(kScanThreads), 0, stream, static_cast<const T*>(logits), vocab,
+                       a.chunks, a.chunk_len, width, a.pm, a.ps, a.pe, a.pv, a.pi, a.err);
   else
-    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 128, ENT>), grid, dim3(kScanThreads), 0,
-                       stream, static_cast<const T*>(logits), vocab, a.chunks, a.chunk_len,
-                       width, a.pm, a.ps, a.pe, a.pv, a.pi, a.err);
+    hipLaunchKernelGGL((draft_row_scan<T, WMAX, VEC, 128, ENT, kScanThreads>), grid,
+                       dim3(kScanThreads), 0, stream, static_cast<const T*>(logits), vocab,
+                       a.chunks, a.chunk_len, width, a.pm, a.ps, a.pe, a.pv, a.pi, a.err);
 }
 
 template <typename T, int WMAX, bool ENT>
