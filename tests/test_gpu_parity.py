@@ -107,6 +107,27 @@ def test_build_tree_bf16_logits_and_budget_edges():
             _assert_tree_equal(g, ref, s, f"bf16 B={Bb} W={W}")
 
 
+
+# Draft-scan shapes the workloads leave out: rows longer than 2^19 logits
+# (128 a thread), and bf16 rows whose length is a multiple of 8 (16-byte
+# loads of 8 logits) on a grid of at most 512 workgroups (512 threads of 16)
+# and on a larger one (256 threads of 32).
+@pytest.mark.parametrize("b,N,V,dtype", [(1, 3, (1 << 19) + 40, "f32"), (1, 2, (1 << 19) + 40, "bf16"),
+                                         (1, 4, 151936, "bf16"), (4, 8, 151936, "bf16")])
+def test_build_tree_scan_shapes(b, N, V, dtype):
+    rng = np.random.default_rng(V + N + b)
+    _say(f"build scan shape b={b} N={N} V={V} {dtype}")
+    L = torch.from_numpy((rng.standard_normal((b, N, V)) * 2.5).astype(np.float32))
+    if dtype == "bf16":
+        L = L.to(torch.bfloat16)
+    roots = torch.from_numpy(rng.integers(0, V, b).astype(np.int32))
+    g = _gpu_build(L, 8, 64, roots)
+    assert g["err"] == 0
+    for s in range(b):
+        ref = O.build_tree(L[s].float().numpy(), 8, 64, int(roots[s]), check_exact=False)
+        _assert_tree_equal(g, ref, s, f"scan b={b} N={N} V={V} {dtype}")
+
+
 # ------------------------------------------------------------------ tree meta
 
 @pytest.mark.parametrize("T,b", [(1, 1), (17, 3), (257, 2), (1024, 1)])
