@@ -24,14 +24,19 @@
 
 namespace jt {
 
-constexpr int kArgmaxThreads = 256;
+constexpr int kArgmaxThreads = 256;       // threads of an argmax workgroup on small grids
+constexpr int kArgmaxThreadsLarge = 512;  // ... and on grids of at least kLargeArgmaxGrid
+// With a grid of many workgroups the wider shape streams the chunks faster
+// (each thread's chain of dependent load rounds is half as long); small grids
+// keep 256 threads.
+constexpr long long kLargeArgmaxGrid = 1024;
 // 16-byte vectors for the streaming loads (read once: non-temporal)
 typedef float f32x4v __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4v __attribute__((ext_vector_type(4)));
 constexpr int kWalkThreads = 1024;
 
-template <typename T, int VEC>
-__global__ __launch_bounds__(kArgmaxThreads) void row_argmax(
+template <typename T, int VEC, int NT>
+__global__ __launch_bounds__(NT) void row_argmax(
     const T* __restrict__ logits, const int32_t* __restrict__ n_nodes, int max_nodes, int vocab,
     int chunks, int chunk_len, float* __restrict__ part_val, int* __restrict__ part_idx,
     int32_t* err) {
@@ -49,11 +54,11 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax(
     // and chunk_len % VEC == 0), and rows start VEC-aligned.  UNR loads per
     // thread are issued before any of them is consumed.
     constexpr int UNR = 4;
-    for (int i0 = begin + threadIdx.x * VEC; i0 < end; i0 += kArgmaxThreads * VEC * UNR) {
+    for (int i0 = begin + threadIdx.x * VEC; i0 < end; i0 += NT * VEC * UNR) {
       float v[UNR][VEC];
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int i = i0 + u * kArgmaxThreads * VEC;
+        const int i = i0 + u * NT * VEC;
         if (i < end) {
           if constexpr (sizeof(T) == 4) {
             const f32x4v f = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(x + i));
@@ -74,7 +79,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax(
       }
 #pragma unroll
       for (int u = 0; u < UNR; ++u) {
-        const int i = i0 + u * kArgmaxThreads * VEC;
+        const int i = i0 + u * NT * VEC;
 #pragma unroll
         for (int k = 0; k < VEC; ++k) {
           const float y = v[u][k];
@@ -84,7 +89,7 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax(
       }
     }
   } else {
-    for (int i = begin + threadIdx.x; i < end; i += kArgmaxThreads) {
+    for (int i = begin + threadIdx.x; i < end; i += NT) {
       const float v = load_as_f32(x, i);
       if (v != v) { bad = true; continue; }
       if (better(v, i, bv, bi)) { bv = v; bi = i; }
@@ -96,13 +101,13 @@ __global__ __launch_bounds__(kArgmaxThreads) void row_argmax(
     const int oi = shfl_xor(bi, o);
     if (better(ov, oi, bv, bi)) { bv = ov; bi = oi; }
   }
-  __shared__ float sv[kArgmaxThreads / kWave];
-  __shared__ int si[kArgmaxThreads / kWave];
+  __shared__ float sv[NT / kWave];
+  __shared__ int si[NT / kWave];
   const int lane = threadIdx.x % kWave, wv = threadIdx.x / kWave;
   if (lane == 0) { sv[wv] = bv; si[wv] = bi; }
   __syncthreads();
   if (threadIdx.x == 0) {
-    for (int w = 1; w < kArgmaxThreads / kWave; ++w)
+    for (int w = 1; w < NT / kWave; ++w)
       if (better(sv[w], si[w], bv, bi)) { bv = sv[w]; bi = si[w]; }
     const size_t o = (static_cast<size_t>(seq) * max_nodes + row) * chunks + c;
     part_val[o] = bv;
@@ -276,9 +281,15 @@ template <typename T, int VEC>
 static void launch_argmax(const void* logits, int batch, int max_nodes, int vocab,
                           const ArgmaxPlan& p, const int32_t* n_nodes, float* pv, int* pi,
                           int32_t* err, hipStream_t stream) {
-  hipLaunchKernelGGL((row_argmax<T, VEC>), dim3(p.chunks, max_nodes, batch), dim3(kArgmaxThreads),
-                     0, stream, static_cast<const T*>(logits), n_nodes, max_nodes, vocab, p.chunks,
-                     p.chunk_len, pv, pi, err);
+  const dim3 grid(p.chunks, max_nodes, batch);
+  if (static_cast<long long>(p.chunks) * max_nodes * batch >= kLargeArgmaxGrid)
+    hipLaunchKernelGGL((row_argmax<T, VEC, kArgmaxThreadsLarge>), grid, dim3(kArgmaxThreadsLarge),
+                       0, stream, static_cast<const T*>(logits), n_nodes, max_nodes, vocab,
+                       p.chunks, p.chunk_len, pv, pi, err);
+  else
+    hipLaunchKernelGGL((row_argmax<T, VEC, kArgmaxThreads>), grid, dim3(kArgmaxThreads), 0, stream,
+                       static_cast<const T*>(logits), n_nodes, max_nodes, vocab, p.chunks,
+                       p.chunk_len, pv, pi, err);
 }
 
 // Scratch of the no-allocation entry point: the argmax partials live in this
