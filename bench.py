@@ -217,6 +217,8 @@ class Verify:
         self.ws_acc = torch.empty(max(1, lib.jt_accept_workspace(b, T, w.vocab)),
                                   dtype=torch.uint8, device=dev)
         self.anc = torch.empty((b, T, (T + 31) // 32), dtype=torch.int32, device=dev)
+        self.tree_out = B._tree_outputs(b, T, dev, True)
+        self.acc_out = B._accept_outputs(b, w.depth_n, dev, None)
         self.out = torch.empty_like(self.d_q)
         self.lse = torch.empty((b, T, w.hq), dtype=torch.float32, device=dev)
         self.stream = torch.cuda.current_stream()
@@ -233,7 +235,7 @@ class Verify:
                 ev[k].append(e)
         mark("s0")
         tree = B.jt_build_tree(self.d_draft, w.width_w, w.budget_b, self.d_root, err=self.err,
-                               workspace=self.ws_build)
+                               workspace=self.ws_build, out=self.tree_out)
         mark("s1")
         B.jt_tree_meta(tree["parent"], tree["n_nodes"], err=self.err, out=self.anc)
         mark("s2")
@@ -242,7 +244,8 @@ class Verify:
                             out=self.out, lse=self.lse, workspace=self.ws_attn)
         mark("s3")
         res = B.jt_accept(self.d_target, w.depth_n, tree["parent"], tree["token"],
-                          tree["depth"], tree["n_nodes"], err=self.err, workspace=self.ws_acc)
+                          tree["depth"], tree["n_nodes"], err=self.err, workspace=self.ws_acc,
+                          out=self.acc_out)
         mark("s4")
         return tree, res
 

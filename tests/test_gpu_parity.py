@@ -534,6 +534,40 @@ def test_step_with_optional_pointers_left_out():
         assert torch.equal(r1, r2)
 
 
+
+def test_build_and_accept_into_preallocated_outputs():
+    """Outputs passed in (out=) receive the same results as freshly allocated
+    ones, and are rejected when their shape or dtype is wrong."""
+    w = WL.WORKLOADS["qwen3_8b_b16"]
+    x = WL.make_inputs(w)
+    d = dev()
+    draft, target, root = x.draft.to(d), x.target.to(d), x.root_token.to(d)
+    t1 = B.jt_build_tree(draft, w.width_w, w.budget_b, root)
+    a1 = B.jt_accept(target, w.depth_n, t1["parent"], t1["token"], t1["depth"], t1["n_nodes"])
+    b, T = draft.shape[0], w.budget_b + 1
+    tout = {k: torch.full((b, T), -7, dtype=torch.int32, device=d) for k in ("parent", "token", "depth")}
+    tout["score"] = torch.full((b, T), 3.0, dtype=torch.float64, device=d)
+    tout["n_nodes"] = torch.full((b,), -7, dtype=torch.int32, device=d)
+    t2 = B.jt_build_tree(draft, w.width_w, w.budget_b, root, out=tout)
+    assert t2 is tout
+    aout = tuple(torch.full(sh, -7, dtype=torch.int32, device=d) for sh in ((b,), (b, w.depth_n), (b,)))
+    a2 = B.jt_accept(target, w.depth_n, t2["parent"], t2["token"], t2["depth"], t2["n_nodes"], out=aout)
+    torch.cuda.synchronize()
+    n = int(t1["n_nodes"][0])
+    for k in ("parent", "token", "depth", "n_nodes"):
+        assert torch.equal(t1[k][..., :n] if k != "n_nodes" else t1[k], t2[k][..., :n] if k != "n_nodes" else t2[k]), k
+    assert torch.equal(t1["score"][:, :n], t2["score"][:, :n])
+    for r1, r2, r3 in zip(a1, a2, aout):
+        assert torch.equal(r1, r2) and r2 is r3
+    bad = dict(tout)
+    bad["parent"] = torch.empty((b, T + 1), dtype=torch.int32, device=d)
+    with pytest.raises(ValueError):
+        B.jt_build_tree(draft, w.width_w, w.budget_b, root, out=bad)
+    with pytest.raises(ValueError):
+        B.jt_accept(target, w.depth_n, t2["parent"], t2["token"], t2["depth"], t2["n_nodes"],
+                    out=(aout[0], aout[1].to(torch.int64), aout[2]))
+
+
 def test_step_on_a_side_stream():
     """Every call enqueues on the caller's stream: the step run on a second
     (default-priority) stream gives the default stream's results."""

@@ -86,12 +86,13 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     return _lib
 
 
+# (the argtypes declare pointers as c_void_p, which takes a plain int or None)
 def _ptr(t):
-    return None if t is None else ctypes.c_void_p(t.data_ptr())
+    return None if t is None else t.data_ptr()
 
 
 def _stream():
-    return ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    return torch.cuda.current_stream().cuda_stream
 
 
 def _check(fn: str, status: int):
@@ -116,20 +117,44 @@ def _workspace(nbytes: int, device):
     return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
 
 
+def _tree_outputs(b: int, T: int, dev, with_score: bool):
+    out = {k: torch.empty((b, T), dtype=torch.int32, device=dev) for k in ("parent", "token", "depth")}
+    out["score"] = torch.empty((b, T), dtype=torch.float64, device=dev) if with_score else None
+    out["n_nodes"] = torch.empty((b,), dtype=torch.int32, device=dev)
+    return out
+
+
+def _check_tree_outputs(out: dict, b: int, T: int):
+    for k in ("parent", "token", "depth"):
+        t = out[k]
+        if t.dtype != torch.int32 or tuple(t.shape) != (b, T) or not t.is_contiguous():
+            raise ValueError(f"out[{k!r}] must be a contiguous int32 [{b}, {T}] tensor")
+    sc = out.get("score")
+    if sc is not None and (sc.dtype != torch.float64 or tuple(sc.shape) != (b, T)
+                           or not sc.is_contiguous()):
+        raise ValueError(f"out['score'] must be a contiguous float64 [{b}, {T}] tensor or None")
+    nn = out["n_nodes"]
+    if nn.dtype != torch.int32 or tuple(nn.shape) != (b,):
+        raise ValueError(f"out['n_nodes'] must be an int32 [{b}] tensor")
+
+
 def jt_build_tree(draft_logits: torch.Tensor, width_w: int, budget_b: int,
                   root_token: torch.Tensor, err: torch.Tensor | None = None,
-                  with_score: bool = True, workspace: torch.Tensor | None = None):
-    """Returns dict(parent, token, depth, score, n_nodes) for a [b, N, V] batch."""
+                  with_score: bool = True, workspace: torch.Tensor | None = None,
+                  out: dict | None = None):
+    """Returns dict(parent, token, depth, score, n_nodes) for a [b, N, V] batch
+    (written into `out` when given: the same keys, preallocated)."""
     lib = load()
     _cuda(draft_logits, "draft_logits")
     b, N, V = draft_logits.shape
     dev = draft_logits.device
     T = budget_b + 1
-    out = {k: torch.empty((b, T), dtype=torch.int32, device=dev) for k in ("parent", "token", "depth")}
-    out["score"] = torch.empty((b, T), dtype=torch.float64, device=dev) if with_score else None
-    out["n_nodes"] = torch.empty((b,), dtype=torch.int32, device=dev)
-    nbytes = lib.jt_build_tree_workspace(b, N, V, width_w, budget_b)
-    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    if out is None:
+        out = _tree_outputs(b, T, dev, with_score)
+    else:
+        _check_tree_outputs(out, b, T)
+    ws = (workspace if workspace is not None
+          else _workspace(lib.jt_build_tree_workspace(b, N, V, width_w, budget_b), dev))
     _check("jt_build_tree", lib.jt_build_tree(
         _ptr(draft_logits), _dtype_code(draft_logits), b, N, V, width_w, budget_b, _ptr(root_token),
         _ptr(out["parent"]), _ptr(out["token"]), _ptr(out["depth"]), _ptr(out["score"]),
@@ -150,11 +175,9 @@ def jt_build_tree_variant(draft_logits: torch.Tensor, width_w: int, budget_b: in
     b, N, V = draft_logits.shape
     dev = draft_logits.device
     T = budget_b + 1
-    out = {k: torch.empty((b, T), dtype=torch.int32, device=dev) for k in ("parent", "token", "depth")}
-    out["score"] = torch.empty((b, T), dtype=torch.float64, device=dev) if with_score else None
-    out["n_nodes"] = torch.empty((b,), dtype=torch.int32, device=dev)
-    nbytes = lib.jt_build_tree_workspace(b, N, V, width_w, budget_b)
-    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    out = _tree_outputs(b, T, dev, with_score)
+    ws = (workspace if workspace is not None
+          else _workspace(lib.jt_build_tree_workspace(b, N, V, width_w, budget_b), dev))
     _check("jt_build_tree_variant", lib.jt_build_tree_variant(
         _ptr(draft_logits), _dtype_code(draft_logits), b, N, V, width_w, budget_b, modes[expand],
         float(entropy_weight), _ptr(root_token), _ptr(out["parent"]), _ptr(out["token"]),
@@ -207,8 +230,8 @@ def jt_tree_attention(q, k_pool, v_pool, n_nodes, prefix_len, page_table, num_pa
         out = torch.empty_like(q)
     if with_lse and lse is None:
         lse = torch.empty((b, T, hq), dtype=torch.float32, device=q.device)
-    nbytes = lib.jt_tree_attention_workspace(b, T, hq, hkv, D, maxp, ps, dt)
-    ws = workspace if workspace is not None else _workspace(nbytes, q.device)
+    ws = (workspace if workspace is not None
+          else _workspace(lib.jt_tree_attention_workspace(b, T, hq, hkv, D, maxp, ps, dt), q.device))
     _check("jt_tree_attention", lib.jt_tree_attention(
         _ptr(q), _ptr(k_pool), _ptr(v_pool), dt, b, T, hq, hkv, D, _ptr(n_nodes),
         _ptr(prefix_len), _ptr(page_table), maxp, int(num_pages), ps, _ptr(anc_mask),
@@ -216,18 +239,30 @@ def jt_tree_attention(q, k_pool, v_pool, n_nodes, prefix_len, page_table, num_pa
     return out, lse
 
 
+def _accept_outputs(b: int, depth_n: int, dev, out):
+    if out is None:
+        return (torch.empty((b,), dtype=torch.int32, device=dev),
+                torch.empty((b, depth_n), dtype=torch.int32, device=dev),
+                torch.empty((b,), dtype=torch.int32, device=dev))
+    alen, anodes, bonus = out
+    for t, nm, shape in ((alen, "accept_len", (b,)), (anodes, "accept_nodes", (b, depth_n)),
+                         (bonus, "bonus_token", (b,))):
+        if t.dtype != torch.int32 or tuple(t.shape) != shape or not t.is_contiguous():
+            raise ValueError(f"{nm} must be a contiguous int32 {list(shape)} tensor")
+    return alen, anodes, bonus
+
+
 def jt_accept(target_logits, depth_n: int, parent, token, depth, n_nodes, err=None,
-              workspace=None):
-    """Returns (accept_len [b], accept_nodes [b, depth_n], bonus_token [b])."""
+              workspace=None, out=None):
+    """Returns (accept_len [b], accept_nodes [b, depth_n], bonus_token [b])
+    (written into `out` when given: that tuple, preallocated)."""
     lib = load()
     _cuda(target_logits, "target_logits")
     b, T, V = target_logits.shape
     dev = target_logits.device
-    alen = torch.empty((b,), dtype=torch.int32, device=dev)
-    anodes = torch.empty((b, depth_n), dtype=torch.int32, device=dev)
-    bonus = torch.empty((b,), dtype=torch.int32, device=dev)
-    nbytes = lib.jt_accept_workspace(b, T, V)
-    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    alen, anodes, bonus = _accept_outputs(b, depth_n, dev, out)
+    ws = (workspace if workspace is not None
+          else _workspace(lib.jt_accept_workspace(b, T, V), dev))
     _check("jt_accept", lib.jt_accept(
         _ptr(target_logits), _dtype_code(target_logits), b, T, V, depth_n, _ptr(parent),
         _ptr(token), _ptr(depth), _ptr(n_nodes), _ptr(alen), _ptr(anodes), _ptr(bonus),
@@ -260,11 +295,9 @@ def jt_accept_margin(target_logits, depth_n: int, parent, token, depth, n_nodes,
     _cuda(target_logits, "target_logits")
     b, T, V = target_logits.shape
     dev = target_logits.device
-    alen = torch.empty((b,), dtype=torch.int32, device=dev)
-    anodes = torch.empty((b, depth_n), dtype=torch.int32, device=dev)
-    bonus = torch.empty((b,), dtype=torch.int32, device=dev)
-    nbytes = lib.jt_accept_workspace(b, T, V)
-    ws = workspace if workspace is not None else _workspace(nbytes, dev)
+    alen, anodes, bonus = _accept_outputs(b, depth_n, dev, None)
+    ws = (workspace if workspace is not None
+          else _workspace(lib.jt_accept_workspace(b, T, V), dev))
     _check("jt_accept_margin", lib.jt_accept_margin(
         _ptr(target_logits), _dtype_code(target_logits), b, T, V, depth_n, _ptr(parent),
         _ptr(token), _ptr(depth), _ptr(n_nodes), float(theta), float(temperature), _ptr(alen),
